@@ -1,0 +1,168 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) paged latent-KV MLA library (libmla.so).
+ *
+ * The library computes absorbed Multi-head Latent Attention over a paged cache
+ * of latent rows.  Every head shares one cached row per token: 512 values of the
+ * compressed latent c_kv followed by 64 values of the decoupled RoPE key
+ * ("LLM inference systems atlas", §06 State architectures and §22 DeepSeek
+ * V2 -> V3; the 512-wide latent: TokenSpeed review page, DeepSeek-V3 entry).  The
+ * key up-projection is already folded into the query and the value up-projection
+ * is applied by the caller afterwards ("absorb + project", TokenSpeed review
+ * page, Attack 1), so for request b, draft token t and head h:
+ *
+ *   K_b[j]   = kv_pool[block_table[b, j / 64], j % 64, 0:576]        j < L_b
+ *   n_vis    = L_b - Sq + t + 1  (causal)   or   L_b  (non-causal)
+ *   s_j      = softmax_scale * (q_nope[b,t,h] . K_b[j][0:512] + q_rope[b,t,h] . K_b[j][512:576])
+ *   lse      = ln(sum_{j < n_vis} exp(s_j))
+ *   O[b,t,h] = sum_{j < n_vis} exp(s_j - lse) * K_b[j][0:512]
+ *
+ * L_b = seq_lens[b] counts every visible row including the Sq new rows, which
+ * the caller has already written into the pool.  Draft t of a speculative verify
+ * sees the prefix and drafts 0..t (atlas §16 Speculative decoding); a prefill
+ * chunk of Sq tokens on a cached prefix sees it the same way (atlas §11 Chunked
+ * prefill).  Sq = 1 is ordinary decode.  Pages are reached only through the
+ * block table (atlas §07 PagedAttention).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tensor pointers are DEVICE pointers to contiguous row-major arrays, aligned
+ *   to 16 bytes.  bf16 values travel as their uint16_t bit patterns.
+ * - The caller owns every buffer (inputs, outputs, workspace).  The library never
+ *   allocates device memory and keeps no per-call state; the only state it holds
+ *   is a per-device cache of the compute-unit count.  Calls on different streams
+ *   are independent as long as they use different workspaces.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   compute entry point only enqueues work and returns; results are ready once the
+ *   stream reaches that point.
+ * - Errors are status codes, never exceptions.  Argument checks run on the host
+ *   before anything is enqueued; on any error nothing is enqueued.
+ * - Data the host cannot see (seq_lens and block_table contents) is checked by the
+ *   kernels: a length outside [Sq, 64 * max_pages_per_seq] or a page id outside
+ *   [0, num_pages) is clamped so that no access leaves the buffers, and a flag is
+ *   raised in the workspace header; mla_read_error_flags() reports it.  Outputs of
+ *   such a call are unspecified.
+ * - Rows at or past L_b in a request's last page and block-table entries past
+ *   ceil(L_b / 64) are never read; they may hold anything (NaN included).
+ * - O and lse are written for every (b, t, h), and may not alias any input.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, non-positive size, NaN scale */
+  MLA_ERR_UNSUPPORTED = -2,  /* page_size != 64, batch or grid beyond the library's limits */
+  MLA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the size query returned */
+  MLA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} mla_status_t;
+
+/* Device-side data faults reported through the workspace header. */
+#define MLA_FLAG_BAD_SEQ_LEN 1u  /* some seq_lens[b] < Sq or > 64 * max_pages_per_seq */
+#define MLA_FLAG_BAD_PAGE_ID 2u  /* some visible block_table entry outside [0, num_pages) */
+
+#define MLA_PAGE_SIZE 64
+#define MLA_NOPE_DIM 512
+#define MLA_ROPE_DIM 64
+#define MLA_MAX_BATCH 1024
+
+/* Text for a status code; never NULL. */
+const char* mla_status_string(int status);
+
+/*
+ * Number of KV partitions ("splits") the decode entry points use when called with
+ * num_partitions = 0, on the current HIP device.  Each partition is a contiguous
+ * run of pages of the batch's concatenated page list; partitions are sized so the
+ * grid covers the device's compute units once.  A result of 1 means no split and
+ * no combine pass.  Returns a status; *num_partitions receives the count.
+ */
+int mla_decode_auto_partitions(int B, int Sq, int H, int max_pages_per_seq,
+                               int* num_partitions);
+
+/*
+ * Workspace bytes a decode or prefill call with these sizes needs (partial
+ * results of the split-KV pass plus a 256-byte header holding the error flags).
+ * num_partitions = 0 means the automatic count on the current device.
+ */
+int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq,
+                              int num_partitions, size_t* bytes);
+
+/*
+ * Speculative-verify / plain decode over the paged latent cache ("Faster kernels,
+ * slower engine", §7.1 Gluon MLA decode: a split-KV pass that materialises
+ * partial results and a second pass that reduces them; the query-length axis is
+ * folded into the head axis to fill the matrix tile: TokenSpeed launch news,
+ * decode-kernel paragraph).  Enqueues the split-KV pass and, when
+ * num_partitions > 1, the log-sum-exp combine pass.
+ *
+ *   q_nope       bf16 [B, Sq, H, 512]   query with the key up-projection absorbed
+ *   q_rope       bf16 [B, Sq, H, 64]    rotated RoPE part of the query
+ *   kv_pool      bf16 [num_pages, 64, 576]  rows [c_kv 0..511 | k_rope 512..575]
+ *   page_size    must be 64
+ *   block_table  int32 [B, max_pages_per_seq]  physical page of each logical page
+ *   seq_lens     int32 [B]   visible rows per request, Sq <= L_b <= 64 * max_pages_per_seq
+ *   softmax_scale  multiplies the whole 576-wide dot product
+ *   causal       1: draft t sees rows j <= L_b - Sq + t;  0: every row j < L_b
+ *   num_partitions  0 = automatic, else the number of KV partitions to use
+ *   O            fp32 [B, Sq, H, 512]   output (written)
+ *   lse          fp32 [B, Sq, H]        natural-log log-sum-exp of the scaled scores
+ *   workspace    device buffer of at least mla_decode_workspace_size() bytes,
+ *                16-byte aligned.  Its first 256 bytes (the error-flag header) must
+ *                be zero before its first use; the rest needs no initialisation.
+ */
+int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+               int64_t num_pages, int page_size,
+               const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+               int B, int Sq, int H, float softmax_scale, int causal, int num_partitions,
+               float* O, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two passes of mla_decode as separate calls, for callers that schedule or
+ * time them apart.  Same arguments and meaning; both calls of one decode must use
+ * the same sizes, num_partitions and workspace.  mla_decode_splitkv writes the
+ * final O/lse of every request that one partition covers whole and partial results
+ * for the others; mla_decode_combine merges those partials (and is a no-op when
+ * the partition count is 1).
+ */
+int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                       int64_t num_pages, int page_size,
+                       const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+                       int B, int Sq, int H, float softmax_scale, int causal, int num_partitions,
+                       float* O, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int mla_decode_combine(const int32_t* seq_lens, int max_pages_per_seq, int B, int Sq, int H,
+                       int num_partitions, float* O, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Chunked prefill on top of a long cached prefix (atlas §11 Chunked prefill;
+ * TokenSpeed launch news, prefill-kernel paragraph).  Sq is the chunk length,
+ * seq_lens[b] = cached prefix + chunk, and the chunk's own latent rows are already
+ * in the pool.  Arguments as for mla_decode; with num_partitions = 0 the folded
+ * chunk rows alone fill the device, so no split and no combine pass is used.
+ */
+int mla_prefill_with_prefix(const uint16_t* q_nope, const uint16_t* q_rope,
+                            const uint16_t* kv_pool, int64_t num_pages, int page_size,
+                            const int32_t* block_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                            int causal, int num_partitions, float* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Waits for `stream`, then copies the workspace header's error flags
+ * (MLA_FLAG_*) to *flags and clears them.  Reading forces a synchronisation, so
+ * callers use it in checked runs and tests, not on the hot path.
+ */
+int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

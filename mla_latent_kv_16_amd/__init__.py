@@ -1,0 +1,23 @@
+"""MI355X (gfx950) paged latent-KV MLA: decode with the draft axis folded into the
+head axis, and chunked prefill over a long cached prefix.
+
+The computation lives in libmla.so (hand-written HIP kernels behind the C ABI in
+include/mla.h); the functions here marshal torch device tensors into that ABI.
+Importing this package loads nothing; the library is opened on first use.
+"""
+from ._binding import (  # noqa: F401
+    BoundDecode,
+    MLAError,
+    LIB_PATH,
+    auto_partitions,
+    decode,
+    decode_combine,
+    decode_splitkv,
+    header_functions,
+    lib,
+    new_workspace,
+    prefill_with_prefix,
+    read_error_flags,
+    status_string,
+    workspace_size,
+)

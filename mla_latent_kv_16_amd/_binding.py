@@ -1,0 +1,257 @@
+"""ctypes binding of libmla.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module turns
+torch tensors into device pointers, picks the current HIP stream, and maps status
+codes to exceptions.  It never computes attention itself and has no CPU fallback:
+if the library is missing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mla.h")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_WORKSPACE = -3
+MLA_ERR_HIP = -4
+MLA_FLAG_BAD_SEQ_LEN = 1
+MLA_FLAG_BAD_PAGE_ID = 2
+PAGE_SIZE = 64
+NOPE_DIM = 512
+ROPE_DIM = 64
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_COMPUTE_ARGS = [_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _i32,
+                 _vp, _vp, _vp, _sz, _vp]
+_SIGNATURES = {
+    "mla_status_string": ([_i32], ctypes.c_char_p),
+    "mla_decode_auto_partitions": ([_i32, _i32, _i32, _i32, ctypes.POINTER(_i32)], _i32),
+    "mla_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
+    "mla_decode": (_COMPUTE_ARGS, _i32),
+    "mla_decode_splitkv": (_COMPUTE_ARGS, _i32),
+    "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
+    "mla_decode_combine": ([_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "mla_read_error_flags": ([_vp, _vp, ctypes.POINTER(ctypes.c_uint32)], _i32),
+}
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions include/mla.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib():
+    """Loads libmla.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_16_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != MLA_OK:
+        raise MLAError(status, where)
+
+
+def auto_partitions(B: int, Sq: int, H: int, max_pages_per_seq: int) -> int:
+    out = _i32(0)
+    _check(lib().mla_decode_auto_partitions(B, Sq, H, max_pages_per_seq, ctypes.byref(out)),
+           "mla_decode_auto_partitions")
+    return out.value
+
+
+def workspace_size(B: int, Sq: int, H: int, max_pages_per_seq: int, num_partitions: int = 0) -> int:
+    out = _sz(0)
+    _check(lib().mla_decode_workspace_size(B, Sq, H, max_pages_per_seq, num_partitions,
+                                           ctypes.byref(out)), "mla_decode_workspace_size")
+    return out.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _expect(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def new_workspace(B, Sq, H, max_pages_per_seq, num_partitions=0, device=None):
+    """Zero-filled workspace of the size the library asks for."""
+    torch = _torch()
+    n = workspace_size(B, Sq, H, max_pages_per_seq, num_partitions)
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def _prep(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace, num_partitions):
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16)
+    if q_nope.dim() != 4:
+        raise ValueError("q_nope must be [B, Sq, H, 512]")
+    B, Sq, H, D = q_nope.shape
+    if D != NOPE_DIM:
+        raise ValueError("q_nope last dim must be 512")
+    _expect(q_nope, "q_nope", bf)
+    _expect(q_rope, "q_rope", bf, (B, Sq, H, ROPE_DIM))
+    if kv_pool.dim() != 3 or kv_pool.shape[1] != PAGE_SIZE or kv_pool.shape[2] != NOPE_DIM + ROPE_DIM:
+        raise ValueError("kv_pool must be [num_pages, 64, 576]")
+    _expect(kv_pool, "kv_pool", bf)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages_per_seq]")
+    _expect(block_table, "block_table", (torch.int32,))
+    _expect(seq_lens, "seq_lens", (torch.int32,), (B,))
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((B, Sq, H, NOPE_DIM), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+    _expect(out, "out", (torch.float32,), (B, Sq, H, NOPE_DIM))
+    _expect(lse, "lse", (torch.float32,), (B, Sq, H))
+    maxp = block_table.shape[1]
+    if workspace is None:
+        workspace = new_workspace(B, Sq, H, maxp, num_partitions, device=dev)
+    _expect(workspace, "workspace", (torch.uint8,))
+    return B, Sq, H, maxp, out, lse, workspace
+
+
+def _compute(fn_name, q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal,
+             num_partitions, out, lse, workspace, stream):
+    B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table, seq_lens,
+                                                out, lse, workspace, num_partitions)
+    fn = getattr(lib(), fn_name)
+    st = fn(_ptr(q_nope), _ptr(q_rope), _ptr(kv_pool), kv_pool.shape[0], PAGE_SIZE,
+            _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H, float(softmax_scale),
+            1 if causal else 0, int(num_partitions), _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel(), _stream_handle(stream))
+    _check(st, fn_name)
+    return out, lse
+
+
+def decode(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
+           num_partitions=0, out=None, lse=None, workspace=None, stream=None):
+    """mla_decode: split-KV pass + combine pass.  Returns (O fp32 [B,Sq,H,512], lse fp32 [B,Sq,H])."""
+    return _compute("mla_decode", q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale,
+                    causal, num_partitions, out, lse, workspace, stream)
+
+
+def decode_splitkv(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
+                   num_partitions=0, out=None, lse=None, workspace=None, stream=None):
+    """mla_decode_splitkv: the split-KV pass alone."""
+    return _compute("mla_decode_splitkv", q_nope, q_rope, kv_pool, block_table, seq_lens,
+                    softmax_scale, causal, num_partitions, out, lse, workspace, stream)
+
+
+def decode_combine(seq_lens, max_pages_per_seq, Sq, H, out, lse, workspace, num_partitions=0,
+                   stream=None):
+    """mla_decode_combine: the log-sum-exp merge of the split-KV partials."""
+    B = seq_lens.shape[0]
+    st = lib().mla_decode_combine(_ptr(seq_lens), max_pages_per_seq, B, Sq, H,
+                                  int(num_partitions), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel(), _stream_handle(stream))
+    _check(st, "mla_decode_combine")
+    return out, lse
+
+
+def prefill_with_prefix(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale,
+                        causal=True, num_partitions=0, out=None, lse=None, workspace=None,
+                        stream=None):
+    """mla_prefill_with_prefix: a chunk of Sq new tokens over its cached prefix."""
+    return _compute("mla_prefill_with_prefix", q_nope, q_rope, kv_pool, block_table, seq_lens,
+                    softmax_scale, causal, num_partitions, out, lse, workspace, stream)
+
+
+def read_error_flags(workspace, stream=None) -> int:
+    """Synchronises the stream and returns (and clears) the kernels' data-fault flags."""
+    out = ctypes.c_uint32(0)
+    _check(lib().mla_read_error_flags(_ptr(workspace), _stream_handle(stream), ctypes.byref(out)),
+           "mla_read_error_flags")
+    return out.value
+
+
+class BoundDecode:
+    """Decode call with its arguments validated and marshalled once.
+
+    For loops that launch the same shapes repeatedly (benchmarks, serving steps):
+    each call is a single foreign-function call into the library.  The tensors are
+    kept alive by this object.
+    """
+
+    def __init__(self, q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
+                 num_partitions=0, out=None, lse=None, workspace=None, stream=None):
+        B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table,
+                                                    seq_lens, out, lse, workspace, num_partitions)
+        self.tensors = (q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace)
+        self.out, self.lse, self.workspace = out, lse, workspace
+        self.num_partitions = int(num_partitions) or auto_partitions(B, Sq, H, maxp)
+        self._args = (_ptr(q_nope), _ptr(q_rope), _ptr(kv_pool), kv_pool.shape[0], PAGE_SIZE,
+                      _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H, float(softmax_scale),
+                      1 if causal else 0, self.num_partitions, _ptr(out), _ptr(lse),
+                      _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        self._cargs = (_ptr(seq_lens), maxp, B, Sq, H, self.num_partitions, _ptr(out), _ptr(lse),
+                       _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        L = lib()
+        self._decode, self._split, self._combine = L.mla_decode, L.mla_decode_splitkv, L.mla_decode_combine
+
+    def __call__(self):
+        _check(self._decode(*self._args), "mla_decode")
+
+    def splitkv(self):
+        _check(self._split(*self._args), "mla_decode_splitkv")
+
+    def combine(self):
+        _check(self._combine(*self._cargs), "mla_decode_combine")

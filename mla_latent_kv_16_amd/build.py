@@ -1,0 +1,68 @@
+"""Builds libmla.so (the gfx950 HIP kernels and their C ABI) in-tree with hipcc.
+
+Usage: python -m mla_latent_kv_16_amd.build [--save-temps DIR]
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libmla.so")
+SOURCES = ["mla_api.hip", "mla_kernels.hip"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # gfx950 packed-fp32 instructions stay off; ordinary float code is used instead
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; ROCm is required to build libmla.so")
+
+
+def build(verbose: bool = True, extra=()) -> str:
+    """Compiles every HIP source into libmla.so next to this file; returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print("[build]", " ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), flush=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    extra = []
+    if len(sys.argv) > 2 and sys.argv[1] == "--save-temps":
+        os.makedirs(sys.argv[2], exist_ok=True)
+        extra = ["-save-temps=obj", "-o"]  # placeholder, handled below
+        cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
+               "--cuda-device-only", "-S"]
+        for s in SOURCES:
+            out = os.path.join(sys.argv[2], s.replace(".hip", ".s"))
+            subprocess.run(cmd + [os.path.join(CSRC, s), "-o", out], check=True)
+            print(out)
+    else:
+        print(build())

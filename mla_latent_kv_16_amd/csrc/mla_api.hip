@@ -1,0 +1,300 @@
+// extern "C" entry points of libmla (declared in include/mla.h): argument checks,
+// partition choice, workspace layout and launches.  No device memory is allocated.
+#include "../../include/mla.h"
+#include "mla_device.h"
+#include "mla_internal.h"
+
+#include <math.h>
+#include <mutex>
+
+namespace {
+
+using namespace mla;
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+// Compute units of the current device (cached per device).
+int cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::call_once(g_cu_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 0;
+    g_cu_count[dev] = n;
+  });
+  if (g_cu_count[dev] <= 0) return MLA_ERR_HIP;
+  *out = g_cu_count[dev];
+  return MLA_OK;
+}
+
+// Geometry of one call: waves per workgroup, M-tile rows, M-tiles per request.
+struct Geometry {
+  int M, waves, mt_rows, n_mt, slot_rows;
+};
+
+int geometry(int B, int Sq, int H, int max_pages, Geometry* g) {
+  if (B < 1 || Sq < 1 || H < 1 || max_pages < 1) return MLA_ERR_INVALID_ARG;
+  if (B > kMaxBatch) return MLA_ERR_UNSUPPORTED;
+  const int64_t M = (int64_t)Sq * H;
+  if (M > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)B * max_pages > 0x7fffffffLL / 2) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages * kPage > 0x7fffffffLL / 2) return MLA_ERR_UNSUPPORTED;
+  g->M = (int)M;
+  g->waves = 4;
+  g->mt_rows = kRowsPerWave * g->waves;
+  g->n_mt = (int)((M + g->mt_rows - 1) / g->mt_rows);
+  g->slot_rows = (int)(M < g->mt_rows ? M : g->mt_rows);
+  return MLA_OK;
+}
+
+// Default partition count: enough (partition x M-tile) workgroups to cover the
+// compute units once, never more partitions than a few pages each can justify.
+int auto_partitions(const Geometry& g, int B, int max_pages, int cus) {
+  const int64_t total_pages = (int64_t)B * max_pages;  // upper bound of the real total
+  int64_t G = cus / g.n_mt;
+  const int64_t by_pages = (total_pages + 3) / 4;       // at least ~4 pages per partition
+  if (G > by_pages) G = by_pages;
+  if (G < 1) G = 1;
+  return (int)G;
+}
+
+int resolve_partitions(const Geometry& g, int B, int max_pages, int requested, int* G) {
+  if (requested < 0) return MLA_ERR_INVALID_ARG;
+  if (requested > 0) {
+    if ((int64_t)requested * g.n_mt > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+    *G = requested;
+    return MLA_OK;
+  }
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != MLA_OK) return st;
+  *G = auto_partitions(g, B, max_pages, cus);
+  return MLA_OK;
+}
+
+size_t workspace_bytes_for(const Geometry& g, int B, int G) {
+  size_t bytes = kHeaderBytes;
+  if (G > 1) {
+    const size_t slots = (size_t)(B + G) * g.n_mt;
+    bytes += slots * g.slot_rows * kNope * sizeof(float);   // partial O
+    bytes += ((slots * g.slot_rows * sizeof(float)) + 255) & ~(size_t)255;  // partial LSE
+  }
+  return bytes;
+}
+
+struct Layout {
+  uint32_t* flags;
+  float* part_o;
+  float* part_lse;
+};
+
+Layout carve(void* ws, const Geometry& g, int B, int G) {
+  Layout l;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  l.flags = reinterpret_cast<uint32_t*>(base);
+  const size_t slots = (size_t)(B + G) * g.n_mt;
+  l.part_o = reinterpret_cast<float*>(base + kHeaderBytes);
+  l.part_lse = reinterpret_cast<float*>(base + kHeaderBytes + slots * g.slot_rows * kNope * 4);
+  return l;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+struct Call {
+  Geometry geo;
+  int G;
+  Layout lay;
+};
+
+// Shared checks of every compute entry point.
+int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+            int64_t num_pages, int page_size, const int32_t* block_table, int max_pages,
+            const int32_t* seq_lens, int B, int Sq, int H, float scale, int causal,
+            int num_partitions, const float* O, const float* lse, void* ws, size_t ws_bytes,
+            Call* call) {
+  if (!q_nope || !q_rope || !kv_pool || !block_table || !seq_lens || !O || !lse)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_pool) || !aligned16(O))
+    return MLA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3) || (reinterpret_cast<uintptr_t>(seq_lens) & 3) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3))
+    return MLA_ERR_INVALID_ARG;
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (num_pages < 1) return MLA_ERR_INVALID_ARG;
+  if (num_pages > (int64_t)1 << 40) return MLA_ERR_UNSUPPORTED;
+  if (!(scale == scale) || isinf(scale)) return MLA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+  int st = geometry(B, Sq, H, max_pages, &call->geo);
+  if (st != MLA_OK) return st;
+  st = resolve_partitions(call->geo, B, max_pages, num_partitions, &call->G);
+  if (st != MLA_OK) return st;
+  if (!ws || !aligned16(ws)) return MLA_ERR_WORKSPACE;
+  if (ws_bytes < workspace_bytes_for(call->geo, B, call->G)) return MLA_ERR_WORKSPACE;
+  call->lay = carve(ws, call->geo, B, call->G);
+  return MLA_OK;
+}
+
+int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
+                  const uint16_t* kv_pool, int64_t num_pages, const int32_t* block_table,
+                  int max_pages, const int32_t* seq_lens, int B, int Sq, int H, float scale,
+                  int causal, float* O, float* lse, hipStream_t stream) {
+  SplitArgs a;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.kv_pool = kv_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.O = O;
+  a.lse = lse;
+  a.part_o = c.lay.part_o;
+  a.part_lse = c.lay.part_lse;
+  a.flags = c.lay.flags;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  a.B = B;
+  a.Sq = Sq;
+  a.H = H;
+  a.M = c.geo.M;
+  a.n_mt = c.geo.n_mt;
+  a.G = c.G;
+  a.slot_rows = c.geo.slot_rows;
+  a.causal = causal;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_splitkv(a, c.geo.waves, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int enqueue_combine(const Call& c, const int32_t* seq_lens, int max_pages, int B, int Sq, int H,
+                    float* O, float* lse, hipStream_t stream) {
+  if (c.G <= 1) return MLA_OK;
+  CombineArgs a;
+  a.seq_lens = seq_lens;
+  a.O = O;
+  a.lse = lse;
+  a.part_o = c.lay.part_o;
+  a.part_lse = c.lay.part_lse;
+  a.flags = c.lay.flags;
+  a.max_pages = max_pages;
+  a.B = B;
+  a.Sq = Sq;
+  a.H = H;
+  a.M = c.geo.M;
+  a.n_mt = c.geo.n_mt;
+  a.G = c.G;
+  a.MT = c.geo.mt_rows;
+  a.slot_rows = c.geo.slot_rows;
+  return launch_combine(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: unsupported size or page size";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown mla status";
+  }
+}
+
+int mla_decode_auto_partitions(int B, int Sq, int H, int max_pages_per_seq, int* num_partitions) {
+  if (!num_partitions) return MLA_ERR_INVALID_ARG;
+  Geometry g;
+  int st = geometry(B, Sq, H, max_pages_per_seq, &g);
+  if (st != MLA_OK) return st;
+  return resolve_partitions(g, B, max_pages_per_seq, 0, num_partitions);
+}
+
+int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq, int num_partitions,
+                              size_t* bytes) {
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  Geometry g;
+  int st = geometry(B, Sq, H, max_pages_per_seq, &g);
+  if (st != MLA_OK) return st;
+  int G = 0;
+  st = resolve_partitions(g, B, max_pages_per_seq, num_partitions, &G);
+  if (st != MLA_OK) return st;
+  *bytes = workspace_bytes_for(g, B, G);
+  return MLA_OK;
+}
+
+int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                       int64_t num_pages, int page_size, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
+                       float softmax_scale, int causal, int num_partitions, float* O, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Call c;
+  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                   workspace_bytes, &c);
+  if (st != MLA_OK) return st;
+  return enqueue_split(c, q_nope, q_rope, kv_pool, num_pages, block_table, max_pages_per_seq,
+                       seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
+                       static_cast<hipStream_t>(stream));
+}
+
+int mla_decode_combine(const int32_t* seq_lens, int max_pages_per_seq, int B, int Sq, int H,
+                       int num_partitions, float* O, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!seq_lens || !O || !lse) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(O) || (reinterpret_cast<uintptr_t>(lse) & 3)) return MLA_ERR_INVALID_ARG;
+  Call c;
+  int st = geometry(B, Sq, H, max_pages_per_seq, &c.geo);
+  if (st != MLA_OK) return st;
+  st = resolve_partitions(c.geo, B, max_pages_per_seq, num_partitions, &c.G);
+  if (st != MLA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < workspace_bytes_for(c.geo, B, c.G)) return MLA_ERR_WORKSPACE;
+  c.lay = carve(workspace, c.geo, B, c.G);
+  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse,
+                         static_cast<hipStream_t>(stream));
+}
+
+int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+               int64_t num_pages, int page_size, const int32_t* block_table,
+               int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
+               float softmax_scale, int causal, int num_partitions, float* O, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  Call c;
+  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                   workspace_bytes, &c);
+  if (st != MLA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = enqueue_split(c, q_nope, q_rope, kv_pool, num_pages, block_table, max_pages_per_seq,
+                     seq_lens, B, Sq, H, softmax_scale, causal, O, lse, s);
+  if (st != MLA_OK) return st;
+  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
+}
+
+int mla_prefill_with_prefix(const uint16_t* q_nope, const uint16_t* q_rope,
+                            const uint16_t* kv_pool, int64_t num_pages, int page_size,
+                            const int32_t* block_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                            int causal, int num_partitions, float* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                    workspace_bytes, stream);
+}
+
+int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {
+  if (!workspace || !flags) return MLA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return MLA_ERR_HIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  const uint32_t zero = 0;
+  if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+    return MLA_ERR_HIP;
+  *flags = v;
+  return MLA_OK;
+}
+
+}  // extern "C"

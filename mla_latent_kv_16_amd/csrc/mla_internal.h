@@ -1,0 +1,47 @@
+// Host <-> kernel interface of libmla: argument blocks and launch helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Arguments of the split-KV attention pass (passed by value as the kernel argument).
+struct SplitArgs {
+  const uint16_t* q_nope;      // [B, M, 512] bf16, M = Sq * H folded rows (m = t * H + h)
+  const uint16_t* q_rope;      // [B, M, 64]
+  const uint16_t* kv_pool;     // [num_pages, 64, 576]
+  const int32_t* block_table;  // [B, max_pages]
+  const int32_t* seq_lens;     // [B]
+  float* O;                    // [B, M, 512]
+  float* lse;                  // [B, M]  natural log
+  float* part_o;               // [slots, slot_rows, 512]  normalised partial outputs
+  float* part_lse;             // [slots, slot_rows]       partial log2-sum-exp2
+  uint32_t* flags;             // workspace header word
+  int64_t num_pages;
+  int max_pages;
+  int B, Sq, H, M;
+  int n_mt;                    // M-tiles per request
+  int G;                       // KV partitions
+  int slot_rows;               // min(M, M-tile rows)
+  int causal;
+  float scale_log2;            // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const int32_t* seq_lens;
+  float* O;
+  float* lse;
+  const float* part_o;
+  const float* part_lse;
+  uint32_t* flags;
+  int max_pages;
+  int B, Sq, H, M;
+  int n_mt, G, MT, slot_rows;
+};
+
+// Launch helpers (defined next to the kernels).  waves is 4 or 8 per workgroup.
+hipError_t launch_splitkv(const SplitArgs& a, int waves, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before touching a device.
+
+Every call below passes an explicit partition count, so no device query runs, and
+each one fails a host check; nothing is ever enqueued.
+"""
+import ctypes
+import math
+import os
+import subprocess
+
+import pytest
+
+import mla_latent_kv_16_amd as mla
+from mla_latent_kv_16_amd import _binding as bnd
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000  # 16-byte aligned host address; never dereferenced by the host checks
+
+
+def test_library_exports_every_header_function():
+    names = mla.header_functions()
+    assert names == sorted([
+        "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_splitkv",
+        "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
+        "mla_status_string"])
+    L = mla.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_c():
+    hdr = os.path.join(os.path.dirname(mla.LIB_PATH), "..", "include", "mla.h")
+    src = f'#include "{os.path.abspath(hdr)}"\nint main(void) {{ return MLA_OK; }}\n'
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-x", "c", "-", "-o", "/dev/null"],
+                         input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_status_strings():
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert mla.status_string(s)
+    assert "unknown" in mla.status_string(12345)
+
+
+def test_workspace_size_explicit_partitions():
+    # one partition: header only; split: (B + G) slots of min(M, 64) rows x (512 + 1) floats
+    assert mla.workspace_size(4, 4, 16, 1025, 1) == 256
+    n = mla.workspace_size(4, 4, 16, 1025, 256)
+    slots, rows = (4 + 256) * 1, 64
+    assert n == 256 + slots * rows * 512 * 4 + (((slots * rows * 4) + 255) // 256) * 256
+    # M = 256 rows -> 4 M-tiles of 64 rows
+    n2 = mla.workspace_size(16, 16, 16, 3200, 64)
+    slots2 = (16 + 64) * 4
+    assert n2 == 256 + slots2 * 64 * 512 * 4 + (((slots2 * 64 * 4) + 255) // 256) * 256
+    # M smaller than a tile: slots hold only M rows
+    n3 = mla.workspace_size(1, 1, 5, 4, 3)
+    assert n3 == 256 + 4 * 5 * 512 * 4 + 256
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(B=0), INVALID), (dict(Sq=0), INVALID), (dict(H=0), INVALID),
+    (dict(max_pages=0), INVALID), (dict(B=1025), UNSUPPORTED), (dict(parts=-1), INVALID),
+])
+def test_workspace_size_rejects(args, code):
+    a = dict(B=2, Sq=2, H=2, max_pages=4, parts=3)
+    a.update(args)
+    out = ctypes.c_size_t(0)
+    st = mla.lib().mla_decode_workspace_size(a["B"], a["Sq"], a["H"], a["max_pages"], a["parts"],
+                                             ctypes.byref(out))
+    assert st == code
+
+
+def _call(name="mla_decode", **over):
+    a = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, num_pages=8, page_size=64,
+             block_table=FAKE, max_pages=4, seq_lens=FAKE, B=1, Sq=1, H=16, scale=0.07,
+             causal=1, parts=2, O=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    fn = getattr(mla.lib(), name)
+    return fn(a["q_nope"], a["q_rope"], a["kv_pool"], a["num_pages"], a["page_size"],
+              a["block_table"], a["max_pages"], a["seq_lens"], a["B"], a["Sq"], a["H"],
+              a["scale"], a["causal"], a["parts"], a["O"], a["lse"], a["ws"], a["ws_bytes"],
+              a["stream"])
+
+
+@pytest.mark.parametrize("name", ["mla_decode", "mla_decode_splitkv", "mla_prefill_with_prefix"])
+@pytest.mark.parametrize("over,code", [
+    (dict(q_nope=None), INVALID), (dict(q_rope=None), INVALID), (dict(kv_pool=None), INVALID),
+    (dict(block_table=None), INVALID), (dict(seq_lens=None), INVALID), (dict(O=None), INVALID),
+    (dict(lse=None), INVALID), (dict(q_nope=FAKE + 8), INVALID), (dict(kv_pool=FAKE + 2), INVALID),
+    (dict(O=FAKE + 4), INVALID), (dict(seq_lens=FAKE + 2), INVALID),
+    (dict(page_size=32), UNSUPPORTED), (dict(page_size=128), UNSUPPORTED),
+    (dict(num_pages=0), INVALID), (dict(scale=math.nan), INVALID), (dict(scale=math.inf), INVALID),
+    (dict(causal=2), INVALID), (dict(B=0), INVALID), (dict(Sq=0), INVALID), (dict(H=-1), INVALID),
+    (dict(max_pages=0), INVALID), (dict(B=4096), UNSUPPORTED), (dict(parts=-3), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws=FAKE + 4), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+    (dict(ws_bytes=255, parts=1), WORKSPACE),
+])
+def test_compute_entry_points_reject_on_host(name, over, code):
+    assert _call(name, **over) == code
+
+
+def test_workspace_one_byte_short_is_rejected():
+    # (a call that passes every host check would enqueue kernels on these fake
+    # pointers, so none is made here)
+    need = mla.workspace_size(1, 1, 16, 4, 2)
+    assert _call(ws_bytes=need - 1) == WORKSPACE
+
+
+def test_combine_rejects_on_host():
+    L = mla.lib()
+    f = L.mla_decode_combine
+    assert f(None, 4, 1, 1, 16, 2, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 1, 1, 16, 2, None, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 1, 1, 16, 2, FAKE + 4, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 0, 1, 16, 2, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 1, 1, 16, 2, FAKE, FAKE, None, 1 << 20, None) == WORKSPACE
+    assert f(FAKE, 4, 1, 1, 16, 2, FAKE, FAKE, FAKE, 10, None) == WORKSPACE
+
+
+def test_read_error_flags_rejects_null():
+    out = ctypes.c_uint32(0)
+    assert mla.lib().mla_read_error_flags(None, None, ctypes.byref(out)) == INVALID
+    assert mla.lib().mla_read_error_flags(FAKE, None, None) == INVALID
+
+
+def test_binding_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bnd, "_lib", None)
+    monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        bnd.lib()
