@@ -30,9 +30,9 @@ int cu_count(int* out) {
   return MLA_OK;
 }
 
-// Geometry of one call: waves per workgroup, M-tile rows, M-tiles per request.
+// Geometry of one call: M-tile rows, M-tiles per request, rows per partial slot.
 struct Geometry {
-  int M, waves, mt_rows, n_mt, slot_rows;
+  int M, mt_rows, n_mt, slot_rows;
 };
 
 int geometry(int B, int Sq, int H, int max_pages, Geometry* g) {
@@ -43,8 +43,7 @@ int geometry(int B, int Sq, int H, int max_pages, Geometry* g) {
   if ((int64_t)B * max_pages > 0x7fffffffLL / 2) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)max_pages * kPage > 0x7fffffffLL / 2) return MLA_ERR_UNSUPPORTED;
   g->M = (int)M;
-  g->waves = 4;
-  g->mt_rows = kRowsPerWave * g->waves;
+  g->mt_rows = kMTile;
   g->n_mt = (int)((M + g->mt_rows - 1) / g->mt_rows);
   g->slot_rows = (int)(M < g->mt_rows ? M : g->mt_rows);
   return MLA_OK;
@@ -163,7 +162,7 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
   a.slot_rows = c.geo.slot_rows;
   a.causal = causal;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return launch_splitkv(a, c.geo.waves, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return launch_splitkv(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int enqueue_combine(const Call& c, const int32_t* seq_lens, int max_pages, int B, int Sq, int H,

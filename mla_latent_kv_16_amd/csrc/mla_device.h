@@ -16,53 +16,64 @@ constexpr int kPage = 64;                      // rows per page
 constexpr int kRowBytes = kRow * 2;            // 1152
 constexpr int kChunks = kRowBytes / 16;        // 72 sixteen-byte chunks per row
 constexpr int kPageBytes = kPage * kRowBytes;  // 73,728
-constexpr int kCombineThreads = 256;           // combine pass: 4 waves, one row each
 constexpr int kMaxBatch = 1024;
 constexpr uint32_t kFlagBadSeqLen = 1u;
 constexpr uint32_t kFlagBadPageId = 2u;
 constexpr int kHeaderBytes = 256;
 
+// Split-KV pass: a workgroup is 4 waves and covers an M-tile of 64 folded query
+// rows.  Waves 2 p and 2 p + 1 own rows 32 p .. 32 p + 31 (one column block of
+// v_mfma_f32_32x32x16_bf16); wave 2 p + c scores contraction half c of the 576-wide
+// rows and accumulates output columns 256 c .. 256 c + 255.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;
+constexpr int kMTile = 64;
+constexpr int kKvBlock = 32;                       // kv rows per MFMA block (S^T tile rows)
+constexpr int kQStepsPerWave = kRow / 16 / 2;      // 18 MFMA k-steps: half the 576-wide row
+constexpr int kColTilesPerWave = kNope / 32 / 2;   // 8 output column tiles of 32
+constexpr int kStageBytes = kKvBlock * kRowBytes;  // 36,864: half a page
+constexpr int kStages = 3;                         // LDS ring depth (two blocks in flight)
+constexpr int kStageCopiesPerWave = 9;             // 16-byte-per-lane copies per wave per stage
+constexpr int kCombineThreads = 256;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
-
-// Each wave owns 16 folded query rows and runs v_mfma_f32_16x16x32_bf16; a
-// workgroup of NW = 4 or 8 waves covers an M-tile of 16 * NW folded rows.
-constexpr int kRowsPerWave = 16;
-constexpr int kQSteps = kRow / 32;     // 18 MFMA k-steps over the 576-wide row
-constexpr int kDBlocks = kNope / 16;   // 32 output column blocks of 16
-constexpr int kBlockRows = 32;         // kv rows per softmax block (2 per page)
 
 // ---- LDS layout of one staged page ------------------------------------------
 // Row r of the page occupies bytes [r * 1152, (r + 1) * 1152).  Its sixteen-byte
 // chunk c sits at chunk position c ^ swz(r); the xor only touches the low three
 // bits, so a chunk never leaves its aligned group of eight (72 = 9 * 8).  With 64
 // four-byte banks, rows r and r + 1 start half a bank row apart, and swz spreads
-// (a) the 16 rows a ds_read_b128 quarter-wave reads at one chunk and (b) the 8 rows
-// x 2 chunks a half-wave of ds_read_b64_tr_b16 reads over distinct banks.
+// (a) the 16 rows a quarter-wave of ds_read_b128 reads at one chunk and (b) the
+// 4 rows x 4 chunks a half-wave of ds_read_b64_tr_b16 reads over distinct banks.
 __device__ __forceinline__ int swz(int r) {
   const int i = (r >> 1) & 7;  // index among same-parity rows of a 16-row block
   return ((i & 1) << 2) | (i & 2) | ((i >> 2) & 1);  // 3-bit bit reversal
 }
 
 // ---- instruction wrappers ---------------------------------------------------
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// 32x32x16 bf16 MFMA.  A [32 x 16]: lane l holds row l % 32, k = 8 (l / 32) + 0..7.
+// B [16 x 32]: lane l holds column l % 32, the same k.  D [32 x 32]: lane l holds
+// column l % 32 and rows 4 (l / 32) + 8 q + c in register 4 q + c.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const uint8_t* lds_base, int byte_off) {
   return *reinterpret_cast<const bf16x8*>(lds_base + byte_off);
 }
 
-// LDS transpose read (gfx950): within each group of 16 lanes, lane 16G + n
-// receives element (n % 4) of the 8-byte words addressed by lanes 16G + 4r + n / 4,
-// r = 0..3.  Addressing four rows with lanes 4r + c gives every lane one column of
-// a 4-row block, i.e. the k-contiguous operand an MFMA needs from a row-major tile.
+// LDS transpose read (gfx950): within each group of 16 lanes, when lane 4 r + c
+// addresses the 8-byte word at columns [4 c, 4 c + 4) of row r (r, c = 0..3), lane n
+// of the group receives column n of rows 0..3: the k-contiguous operand an MFMA
+// needs from a row-major tile.
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* lds_base, int byte_off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4_t*)(lds_base + byte_off));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(lds_base + byte_off));
 }
 
 // LDS byte address of a pointer into __shared__ memory.
@@ -83,12 +94,10 @@ __device__ __forceinline__ void dma16(const void* sbase, int voff, uint32_t lds)
                : "memory");
 }
 
-// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Reductions over the four lanes l % 16 + 16 k that hold one S^T column.
 // v_permlane32_swap(x, x) leaves x[l % 32] in the first result and x[32 + l % 32]
-// in the second, on every lane.
+// in the second, on every lane: the two halves of a 32x32 MFMA column.
 __device__ __forceinline__ float pair32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -96,19 +105,6 @@ __device__ __forceinline__ float pair32_max(float x) {
 __device__ __forceinline__ float pair32_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor16_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 16, 64));
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-  return x + __shfl_xor(x, 16, 64);
-}
-
-__device__ __forceinline__ bf16x8 pack_bf16(const float* v) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(v[i]);
-  return r;
 }
 
 // ---- KV partition plan -------------------------------------------------------

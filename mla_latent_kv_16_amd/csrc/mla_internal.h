@@ -40,8 +40,8 @@ struct CombineArgs {
   int n_mt, G, MT, slot_rows;
 };
 
-// Launch helpers (defined next to the kernels).  waves is 4 or 8 per workgroup.
-hipError_t launch_splitkv(const SplitArgs& a, int waves, hipStream_t stream);
+// Launch helpers (defined next to the kernels).
+hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -1,14 +1,17 @@
 // gfx950 kernels of the paged latent-KV MLA library.
 //
-//  splitkv_kernel<NW>  one workgroup = (KV partition g, M-tile mt) with NW waves.
-//                      It walks the pages of its partition (possibly across
-//                      request boundaries), staging each 64-row page into LDS
-//                      with direct global->LDS copies; every wave scores its 16
-//                      folded query rows against the staged rows (S^T = K Q^T on
-//                      bf16 MFMA), runs the online softmax and accumulates
-//                      O += P V.  A request the partition covers whole gets its
-//                      final O/LSE; otherwise the piece writes a normalised
-//                      partial and its log-sum-exp.
+//  splitkv_kernel      one workgroup = (KV partition g, M-tile of 64 folded query
+//                      rows), four waves.  It walks the pages of its partition
+//                      (possibly across request boundaries) as 32-row blocks,
+//                      staged into an LDS ring with direct global->LDS copies two
+//                      blocks ahead.  A pair of waves owns 32 query rows: each
+//                      wave scores half of the 576-wide contraction (S^T = K Q^T
+//                      on v_mfma_f32_32x32x16_bf16, its half of Q resident in
+//                      registers), the pair swaps halves through LDS, both run the
+//                      online softmax on the full scores, and each accumulates
+//                      O += P V for its 256 of the 512 output columns.  A request
+//                      the partition covers whole gets its final O/LSE; otherwise
+//                      the piece writes a normalised partial and its log-sum-exp.
 //  combine_kernel      merges the partials of split requests by log-sum-exp.
 //
 // Split-KV with materialised partials and a reduction pass is the decode design
@@ -16,9 +19,10 @@
 // decode).  Folding the draft axis into the head axis so that Sq x H rows fill the
 // matrix tile is TokenSpeed's decode-kernel idea (launch news, decode-kernel
 // paragraph; review page, Attack 1: H_eff = num_heads x q_seqlen).  On gfx950 the
-// folded rows form the N axis of S^T = K Q^T: the staged page is the MFMA A
-// operand read straight from LDS, Q stays in registers for the whole walk, and
-// the S^T accumulator layout is already the A operand layout of P V.
+// folded rows form the N axis of S^T = K Q^T, so the staged page is the MFMA A
+// operand read straight from LDS, a query row's 64 scores of a page sit in two
+// lanes (row reductions are one permlane32 swap), and the S^T accumulator is
+// already the A-operand layout of O = P V.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -26,273 +30,322 @@
 
 namespace mla {
 
-// Skip the O rescale until a row's running max has grown by more than this many
-// powers of two.  Until then p = exp2(s - m_ref) stays below 2^32, far inside the
-// range of bf16 P and of the fp32 sums (at most 2^32 * 2^21 rows); the final
-// normalisation uses the same m_ref, so the result does not depend on when (or
-// whether) rescales happen.  Normally only a row's first visible block sets m_ref;
-// the rescale is left for adversarial score ranges and runs outside the hot loop.
+// A row's exp2 reference m_ref is the max of its first visible block and then stays
+// fixed while the piece is walked, so p = exp2(s - m_ref) needs no running rescale
+// of O inside the loop as long as later scores stay below m_ref + kLazyRescale
+// (p < 2^32, far inside the range of bf16 P and of the fp32 sums).  Every block
+// also tracks the row's true max; if any row of the workgroup broke the bound, the
+// piece is walked a second time with m_ref set to that max, where no score can
+// exceed it.  The final normalisation uses the same m_ref as the sums, so the
+// result does not depend on which reference was used.
 constexpr float kLazyRescale = 32.0f;
+constexpr int kBtCache = 256;  // block-table entries cached in LDS per refill
+constexpr float kLn2 = 0.69314718055994531f;
 
 struct WaveState {
-  f32x4 acc[kDBlocks];  // O: rows 4 * (lane / 16) + i, columns 16 * db + lane % 16
-  float m_ref;          // running max (log2 domain) of this lane's query row
-  float l_run;          // this lane's share of that row's exp2 sum (gives the LSE)
-  float l_bf;           // the same sum over the bf16-rounded P that enters P V
-  float m_pending;      // max that triggered a rescale request
+  f32x16 acc[kColTilesPerWave];  // O: column 256 c + 32 ct + lane % 32, rows acc_row(lane, i)
+  float m_ref;                   // exp2 reference (log2 domain) of query row lane % 32
+  float m_seen;                  // max score of that row so far
+  float l_run;                   // this lane's share of that row's exp2 sum (gives the LSE)
+  float l_bf;                    // the same sum over the bf16-rounded P that enters P V
 };
 
-// Query row (0..15 within the wave) of element i of an O accumulator.
-__device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4) + i; }
+// Row (0..31) of register i of a 32x32 MFMA accumulator held by `lane`; the same map
+// gives the kv row of an S^T register and the query row of an O register.
+__device__ __forceinline__ int acc_row(int lane, int i) {
+  return 4 * (lane >> 5) + 8 * (i >> 2) + (i & 3);
+}
 
-__device__ __forceinline__ float row_max(float x) { return pair32_max(xor16_max(x)); }
-__device__ __forceinline__ float row_sum(float x) { return pair32_sum(xor16_sum(x)); }
-
-// ---- staging a page into LDS ----------------------------------------------------
-// The page is 8 groups of 8 rows; group j is 576 sixteen-byte chunks, i.e. 9 copies
-// of 64 lanes x 16 bytes.  Wave w copies groups w, w + NW, ...  LDS chunk position
-// q of a group receives the global chunk the swizzled layout wants there.  The
-// swizzle of row 8 j + rr depends on j only through j % 2, and every group a wave
-// copies has the same parity, so the 9 per-lane source offsets (relative to the
-// group's first row) are fixed per wave.
+// ---- staging a half page into LDS -----------------------------------------------
+// A stage is 32 rows = 4 groups of 8 rows; wave w copies group w: 576 sixteen-byte
+// chunks, i.e. 9 copies of 64 lanes x 16 bytes.  LDS chunk position q of the group
+// receives the global chunk the swizzled layout wants there; the swizzle of a row
+// depends only on its index mod 16, so the half of the page does not matter.
+// Rows at or past `valid` re-read the stage's last valid row (finite data whose
+// scores are masked), so nothing past the request's length is touched.
 struct StageOffsets {
-  int off[9];
+  int off[kStageCopiesPerWave];  // per-lane source offset of copy i, rows 8 w .. 8 w + 7
 };
 
 __device__ __forceinline__ StageOffsets stage_offsets() {
   StageOffsets so;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < kStageCopiesPerWave; ++i) {
     const int q = i * 64 + lane;
     const int rr = q / kChunks;
     const int pos = q - rr * kChunks;
-    so.off[i] = rr * kRowBytes + ((pos ^ swz(8 * wave + rr)) << 4);
+    const int r = 8 * wave + rr;
+    so.off[i] = r * kRowBytes + ((pos ^ swz(r)) << 4);
   }
   return so;
 }
 
-// Stage logical page `pg` of request b into `stage`.  Rows at or past `valid` re-read
-// the page's last valid row (finite data whose scores are masked), so nothing past
-// L_b is touched.
-template <int NW>
-__device__ __forceinline__ void stage_page(const SplitArgs& a, const StageOffsets& so,
-                                           uint8_t* stage, int b, int pg, int L) {
+__device__ __forceinline__ void stage_half(const uint16_t* kv_pool, const StageOffsets& so,
+                                           uint8_t* stage, int phys, int half, int valid) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int phys = a.block_table[(size_t)b * a.max_pages + pg];
-  if (phys < 0 || (int64_t)phys >= a.num_pages) {
-    if (threadIdx.x == 0) atomicOr(a.flags, kFlagBadPageId);
-    phys = 0;
-  }
   phys = __builtin_amdgcn_readfirstlane(phys);
-  const int valid = min(kPage, L - pg * kPage);
-  const uint8_t* page = reinterpret_cast<const uint8_t*>(a.kv_pool) + (size_t)phys * kPageBytes;
-  const uint32_t lds0 = lds_addr(stage);
-  if (valid == kPage) {
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(kv_pool) + (size_t)phys * kPageBytes +
+                       half * kStageBytes;
+  const int row0 = 8 * wave;
+  const uint32_t dst = lds_addr(stage) + row0 * kRowBytes;
+  if (row0 + 8 <= valid) {
 #pragma unroll
-    for (int j = 0; j < 8 / NW; ++j) {
-      const int row0 = 8 * (wave + NW * j);
-      const uint8_t* src = page + row0 * kRowBytes;
-      const uint32_t dst = lds0 + row0 * kRowBytes;
-#pragma unroll
-      for (int i = 0; i < 9; ++i) dma16(src, so.off[i], dst + i * 1024);
-    }
+    for (int i = 0; i < kStageCopiesPerWave; ++i) dma16(src, so.off[i], dst + i * 1024);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8 / NW; ++j) {
-      const int row0 = 8 * (wave + NW * j);
-      const uint32_t dst = lds0 + row0 * kRowBytes;
-#pragma unroll
-      for (int i = 0; i < 9; ++i) {
-        const int q = i * 64 + lane;
-        const int rr = q / kChunks;
-        const int pos = q - rr * kChunks;
-        const int r = row0 + rr;
-        const int rs = min(r, valid - 1);
-        dma16(page, rs * kRowBytes + ((pos ^ swz(r)) << 4), dst + i * 1024);
-      }
+    for (int i = 0; i < kStageCopiesPerWave; ++i) {
+      const int q = i * 64 + lane;
+      const int rr = q / kChunks;
+      const int pos = q - rr * kChunks;
+      const int r = row0 + rr;
+      const int rs = min(r, valid - 1);
+      dma16(src, rs * kRowBytes + ((pos ^ swz(r)) << 4), dst + i * 1024);
     }
   }
 }
 
 // ---- per-lane LDS read bases ---------------------------------------------------
 // Every LDS address of the walk is (per-lane base) + (compile-time offset): the xor
-// swizzle touches only the low three chunk bits, so for each k-step or column
-// block the per-lane part takes one of a few values and the rest is an immediate.
+// swizzle touches only the low three chunk bits, so for each k-step or column tile
+// the per-lane part takes one of a few values and the rest is an immediate.
 struct ReadBases {
-  int a[2];   // S^T A operand (kv rows), MFMA k-step kk with kk % 2 == index
-  int tr[4];  // V operand (transposed), column block db with db % 4 == index
+  int k[4];     // S^T A operand: kv row lane % 32, local k-step kk with kk % 4 == index
+  int v[2][2];  // O B operand (V read transposed): [second 4-row group][column tile % 2]
 };
 
-__device__ __forceinline__ ReadBases read_bases() {
+// c: this wave's half of the 576-wide contraction (k-steps 18 c .. 18 c + 17) and
+// of the 512 output columns (256 c .. 256 c + 255).
+__device__ __forceinline__ ReadBases read_bases(int c) {
   const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
   ReadBases rb;
-  // A operand of S^T = K Q^T: lane reads kv row lane % 16, k slice 8 * (lane / 16)
-  const int row = lane & 15, c0 = lane >> 4, sw = swz(row);
+  // A operand of S^T = K Q^T: lane reads kv row lane % 32 at k = 16 (18 c + kk) + 8 h,
+  // i.e. chunk 36 c + 2 kk + h = 8 (kk / 4) + C with C = 36 c + 2 (kk % 4) + h
+  const int r = lane & 31, sw = swz(r);
 #pragma unroll
-  for (int k = 0; k < 2; ++k) rb.a[k] = row * kRowBytes + (((4 * k + c0) ^ sw) << 4);
-  // B operand of O += P V: lanes 4 r + c of each 16-lane group address kv row
-  // 4 * group + r (and that + 16) at columns 16 * db + 4 c
-  const int ra0 = 4 * (lane >> 4) + ((lane & 15) >> 2);
-  const int cw = (lane & 3) >> 1;
-  const int swa = swz(ra0);  // rows ra0 + 16 share it
+  for (int j = 0; j < 4; ++j) {
+    const int C = 36 * c + 2 * j + h;
+    rb.k[j] = r * kRowBytes + (((C & ~7) | ((C & 7) ^ sw)) << 4);
+  }
+  // B operand of O = P V: in 16-lane group G, lane 4 r4 + c4 addresses kv row
+  // 16 ks + 8 second + 4 h + r4 at columns 256 c + 32 ct + 16 (G % 2) + 4 c4
+  const int G = lane >> 4, n = lane & 15, r4 = n >> 2, c4 = n & 3;
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
-    rb.tr[p] = ra0 * kRowBytes + (((2 * p + cw) ^ swa) << 4) + (lane & 1) * 8;
+  for (int second = 0; second < 2; ++second) {
+    const int row = 8 * second + 4 * h + r4;
+    const int sw2 = swz(row);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      rb.v[second][par] = row * kRowBytes + 512 * c +
+                          (((4 * par + 2 * (G & 1) + (c4 >> 1)) ^ sw2) << 4) + 8 * (c4 & 1);
+  }
   return rb;
 }
 
-// One block of 32 kv rows, starting at byte `blk` of LDS, against this wave's query
-// rows: S^T = K Q^T, mask, online softmax, O += P V.  Returns false, with O and the
-// sums untouched, when a row with a finite running max needs a rescale; the caller
-// applies it and runs the block again.
+// One block of 32 kv rows (stage `blk` in LDS) against this wave pair's 32 query
+// rows.  Each wave of the pair computes S^T = K Q^T over its half of the contraction,
+// the halves are exchanged through `xs` (this wave's slot; the partner's is the
+// neighbouring one), then both waves run the same softmax step on the full scores
+// and accumulate O += P V for their 256 columns.  `lim` is the number of leading
+// rows of the block this lane's query row may see.  Contains one workgroup
+// barrier: every wave of the workgroup must call it for the same blocks.
 //
 // LDS operand reads run a fixed distance ahead of the MFMAs that consume them and
 // sched_barrier pins that order, so the compiler neither serialises each read with
 // its MFMA nor hoists every read (and its registers) to the top.
-__device__ __forceinline__ bool attend_block(const uint8_t* blk, const ReadBases& rb,
-                                             const bf16x8* qreg, WaveState& ws, int lim,
-                                             float scale_log2) {
+__device__ __forceinline__ void attend_block(const uint8_t* blk, const ReadBases& rb,
+                                             const bf16x8* qreg, f32x4* xs, int partner_off,
+                                             WaveState& ws, int lim, float scale_log2) {
   const int lane = threadIdx.x & 63;
-  constexpr int NQK = 2 * kQSteps;  // 36 MFMAs: 2 sub-blocks of 16 kv rows x 18 k-steps
-  constexpr int DQ = 4;             // A-operand reads in flight
-  constexpr int DV = 2;             // V-operand read pairs in flight
+  constexpr int DQ = 4;                      // A-operand reads in flight
+  constexpr int DV = 2;                      // V-operand read pairs in flight
+  constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
 
-  auto qk_off = [&](int step) {  // step = 2 kk + jj
-    const int kk = step >> 1, jj = step & 1;
-    return rb.a[kk & 1] + jj * 16 * kRowBytes + (kk >> 1) * 128;
-  };
-  auto pv_off = [&](int db, int which) {  // which: 0 = rows ra, 1 = rows ra + 16
-    return rb.tr[db & 3] + (db >> 2) * 128 + which * 16 * kRowBytes;
+  const uint8_t* kbase[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kbase[j] = blk + rb.k[j];
+  const uint8_t* vbase[2][2];
+#pragma unroll
+  for (int sd = 0; sd < 2; ++sd)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) vbase[sd][par] = blk + rb.v[sd][par];
+  auto qk_read = [&](int kk) { return lds_read_b128(kbase[kk & 3], (kk >> 2) * 128); };
+  // t = 8 ks + ct, ks-major so consecutive MFMAs use different accumulators
+  auto pv_read = [&](int t, int sd) {
+    const int ks = t >> 3, ct = t & 7;
+    return lds_read_tr(vbase[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
   };
 
-  // ---- S^T = K Q^T; lane holds kv rows 16 jj + 4 (lane / 16) + i of column lane % 16
-  f32x4 s[2] = {f32x4{}, f32x4{}};
+  // ---- S^T = K Q^T over this wave's half of the 576-wide rows
+  f32x16 s = {};
   bf16x8 abuf[DQ];
 #pragma unroll
-  for (int u = 0; u < DQ; ++u) abuf[u] = lds_read_b128(blk, qk_off(u));
+  for (int u = 0; u < DQ; ++u) abuf[u] = qk_read(u);
 #pragma unroll
-  for (int step = 0; step < NQK; ++step) {
-    s[step & 1] = mfma(abuf[step % DQ], qreg[step >> 1], s[step & 1]);
-    if (step + DQ < NQK) abuf[step % DQ] = lds_read_b128(blk, qk_off(step + DQ));
+  for (int kk = 0; kk < kQStepsPerWave; ++kk) {
+    s = mfma32(abuf[kk % DQ], qreg[kk], s);
+    if (kk + DQ < kQStepsPerWave) abuf[kk % DQ] = qk_read(kk + DQ);
     __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- exchange the halves: own + partner is the same sum on both waves
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    xs[j * 64 + lane] = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 o = xs[partner_off + j * 64 + lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[4 * j + e] += o[e];
   }
 
   // first V operands go out before the softmax, which does not need them
   bf16x4 vb0[DV], vb1[DV];
 #pragma unroll
   for (int u = 0; u < DV; ++u) {
-    vb0[u] = lds_read_tr(blk, pv_off(u, 0));
-    vb1[u] = lds_read_tr(blk, pv_off(u, 1));
+    vb0[u] = pv_read(u, 0);
+    vb1[u] = pv_read(u, 1);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- scale into the log2 domain, causal / length mask
-  float x[8];
+  f32x16 x = s * scale_log2;
+  if (__builtin_amdgcn_ballot_w64(lim < kKvBlock)) {
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[jj * 4 + i] = s[jj][i] * scale_log2;
-  if (__builtin_amdgcn_ballot_w64(lim < kBlockRows)) {
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (jj * 16 + 4 * (lane >> 4) + i >= lim) x[jj * 4 + i] = -INFINITY;
+    for (int i = 0; i < 16; ++i)
+      if (acc_row(lane, i) >= lim) x[i] = -INFINITY;
   }
 
-  // ---- online softmax
-  float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mloc = row_max(mloc);
-  const float m_new = fmaxf(ws.m_ref, mloc);
-  if (__builtin_amdgcn_ballot_w64(m_new > ws.m_ref + kLazyRescale)) {
-    // rows still at -inf have O = 0 and l = 0 and just adopt the new max
-    if (__builtin_amdgcn_ballot_w64(ws.m_ref != -INFINITY && m_new > ws.m_ref + kLazyRescale)) {
-      ws.m_pending = m_new;
-      return false;
-    }
-    ws.m_ref = m_new;
-  }
+  // ---- softmax step (a query row's 32 scores sit in lanes l and l + 32)
+  float mloc = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+  mloc = pair32_max(mloc);
+  ws.m_seen = fmaxf(ws.m_seen, mloc);
+  if (ws.m_ref == -INFINITY) ws.m_ref = mloc;  // a row's first visible block sets it
   const float m_use = (ws.m_ref == -INFINITY) ? 0.0f : ws.m_ref;
   float psum = 0.0f;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    x[v] = __builtin_amdgcn_exp2f(x[v] - m_use);
-    psum += x[v];
+  for (int i = 0; i < 16; ++i) {
+    x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+    psum += x[i];
   }
   ws.l_run += psum;
 
-  // P as the A operand of O += P V: lane holds query row lane % 16 and, as its 8 k
-  // values, kv rows 4 (lane / 16) + 0..3 and 16 + 4 (lane / 16) + 0..3.  The V
-  // operand is read in that same kv-row order.  O is later divided by the sum of
-  // the rounded weights it was built from, so a row dominated by one key returns
-  // that key's c_kv up to fp32 rounding rather than up to bf16 rounding.
-  const bf16x8 pop = pack_bf16(x);
+  // P as the A operand of O = P V: for k-step ks lane holds query row lane % 32 and
+  // S^T registers 8 ks .. 8 ks + 7, i.e. kv rows 16 ks + 4 h + 0..3 and
+  // 16 ks + 8 + 4 h + 0..3; the V operand is read in that same kv-row order.  O is
+  // later divided by the sum of the rounded weights it was built from, so a row
+  // dominated by one key returns that key's c_kv up to fp32 rounding rather than
+  // up to bf16 rounding.
+  bf16x8 pa[2];
   float pbf = 0.0f;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) pbf += static_cast<float>(pop[v]);
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pa[ks][k] = static_cast<__bf16>(x[8 * ks + k]);
+      pbf += static_cast<float>(pa[ks][k]);
+    }
   ws.l_bf += pbf;
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- O += P V, V = c_kv columns of the same staged rows, read transposed
+  // ---- O += P V, V = this wave's 256 c_kv columns of the same staged rows
 #pragma unroll
-  for (int db = 0; db < kDBlocks; ++db) {
-    const int u = db % DV;
+  for (int t = 0; t < NPV; ++t) {
+    const int u = t % DV;
     const bf16x8 bv = {vb0[u][0], vb0[u][1], vb0[u][2], vb0[u][3],
                        vb1[u][0], vb1[u][1], vb1[u][2], vb1[u][3]};
-    ws.acc[db] = mfma(pop, bv, ws.acc[db]);
-    if (db + DV < kDBlocks) {
-      vb0[u] = lds_read_tr(blk, pv_off(db + DV, 0));
-      vb1[u] = lds_read_tr(blk, pv_off(db + DV, 1));
+    ws.acc[t & 7] = mfma32(pa[t >> 3], bv, ws.acc[t & 7]);
+    if (t + DV < NPV) {
+      vb0[u] = pv_read(t + DV, 0);
+      vb1[u] = pv_read(t + DV, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  return true;
 }
 
-// Rare path: scale O rows and sums by exp2(m_ref - m_pending) for rows whose finite
-// max grew past the lazy threshold, and adopt the new max.
-__device__ __forceinline__ void apply_rescale(WaveState& ws) {
+// Normalises this wave's 32 rows x 256 columns and writes them: final O / LSE when
+// the piece is the whole request, else a partial slot.  l_tot and l_bf are full row
+// sums (per lane, row lane % 32).
+__device__ __forceinline__ void write_rows(const SplitArgs& a, const WaveState& ws, float l_tot,
+                                           float l_bf, int b, int m_slice, int row_in_tile,
+                                           int c, bool whole, int slot) {
   const int lane = threadIdx.x & 63;
-  const bool grow = ws.m_pending > ws.m_ref;
-  const float alpha =
-      (grow && ws.m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(ws.m_ref - ws.m_pending) : 1.0f;
-  if (grow) ws.m_ref = ws.m_pending;
-  ws.l_run *= alpha;
-  ws.l_bf *= alpha;
-  float al[4];
+  const int M = a.M;
+  const bool seen = l_tot > 0.0f;
+  const float inv = (seen && l_bf > 0.0f) ? 1.0f / l_bf : 0.0f;
+  const float lse2 = seen ? ws.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+  float* base = whole ? a.O + ((size_t)b * M + m_slice) * kNope
+                      : a.part_o + ((size_t)slot * a.slot_rows + row_in_tile) * kNope;
+  const int col = 256 * c + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, acc_row(lane, i), 64);
+  for (int i = 0; i < 16; ++i) {
+    const int r = acc_row(lane, i);
+    const float inv_i = __shfl(inv, r, 64);
+    if (m_slice + r < M) {
+      float* rowp = base + (size_t)r * kNope + col;
 #pragma unroll
-  for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ws.acc[db][i] *= al[i];
+      for (int ct = 0; ct < kColTilesPerWave; ++ct) rowp[32 * ct] = ws.acc[ct][i] * inv_i;
+    }
+  }
+  if (c == 0 && lane < 32 && m_slice + lane < M) {
+    if (whole)
+      a.lse[(size_t)b * M + m_slice + lane] = lse2 * kLn2;
+    else
+      a.part_lse[(size_t)slot * a.slot_rows + row_in_tile + lane] = lse2;
+  }
 }
 
-template <int NW>
-__device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* kv_lds, int b, int mt,
-                                          int lo, int hi, bool whole, int slot) {
-  constexpr int MT = kRowsPerWave * NW;
+// Fill the LDS block-table cache with the physical pages of logical pages
+// [first, min(first + kBtCache, end)) of request b; out-of-range ids are clamped
+// to page 0 and flagged.  Ends in a barrier.
+__device__ __forceinline__ void fill_bt_cache(const SplitArgs& a, int* bt_cache, int b, int first,
+                                              int end) {
+  const int idx = first + (int)threadIdx.x;
+  if (threadIdx.x < kBtCache && idx < end) {
+    int phys = a.block_table[(size_t)b * a.max_pages + idx];
+    if (phys < 0 || (int64_t)phys >= a.num_pages) {
+      atomicOr(a.flags, kFlagBadPageId);
+      phys = 0;
+    }
+    bt_cache[threadIdx.x] = phys;
+  }
+  __syncthreads();
+}
+
+// One piece: logical pages [lo, hi) of request b against M-tile mt.  The pages are
+// walked as 32-row blocks through a ring of kStages half-page stages, two blocks
+// ahead of the one being scored.
+__device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32x4* xbuf,
+                                          int* bt_cache, int* redo_flag, int b, int mt, int lo,
+                                          int hi, bool whole, int slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = wave >> 1, c = wave & 1;  // row slice of the M-tile; contraction / column half
   const int M = a.M;
-  const int m_wave = mt * MT + wave * kRowsPerWave;
-  const int m_q = m_wave + (lane & 15);  // the query row this lane scores
+  const int m_slice = mt * kMTile + p * kRowsPerWave;
+  const int m_q = m_slice + (lane & 31);  // the query row this lane scores
   const bool q_ok = m_q < M;
   const int L = clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
   const int t = q_ok ? m_q / a.H : 0;
   const int n_vis = a.causal ? L - a.Sq + t + 1 : L;
+  // rows the M-tile's last query row sees: blocks past it are skipped by every wave
+  const int m_last = min(M, (mt + 1) * kMTile) - 1;
+  const int n_vis_max = a.causal ? L - a.Sq + m_last / a.H + 1 : L;
+  const int nb = max(0, min(2 * (hi - lo), (n_vis_max + kKvBlock - 1) / kKvBlock - 2 * lo));
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query row m_q,
-  // k = 32 kk + 8 (lane / 16) + 0..7
-  bf16x8 qreg[kQSteps];
+  // k = 16 (18 c + kk) + 8 (lane / 32) + 0..7
+  bf16x8 qreg[kQStepsPerWave];
   {
-    const int kq = 8 * (lane >> 4);
+    const int kh = 8 * (lane >> 5);
     const size_t qrow = (size_t)b * M + (q_ok ? m_q : 0);
 #pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk) {
-      const int k0 = kk * 32 + kq;
+    for (int kk = 0; kk < kQStepsPerWave; ++kk) {
+      const int k0 = (kQStepsPerWave * c + kk) * 16 + kh;
       bf16x8 v;
       if (k0 < kNope)
         v = *reinterpret_cast<const bf16x8*>(a.q_nope + qrow * kNope + k0);
@@ -303,76 +356,75 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* kv_lds, i
   }
 
   WaveState ws;
-#pragma unroll
-  for (int db = 0; db < kDBlocks; ++db) ws.acc[db] = f32x4{};
-  ws.m_ref = -INFINITY;
-  ws.l_run = 0.0f;
-  ws.l_bf = 0.0f;
-  ws.m_pending = -INFINITY;
-
+  ws.m_seen = -INFINITY;
+  const ReadBases rb = read_bases(c);
   const StageOffsets so = stage_offsets();
-  const ReadBases rb = read_bases();
-  stage_page<NW>(a, so, kv_lds, b, lo, L);
-  // Blocks of 32 kv rows, two per staged page.  The inner loop is the hot path; it
-  // leaves only when a rescale is due, which is applied before resuming at the same
-  // block (whose page is already staged and published).
-  int blk = 2 * lo;
-  int resumed = -1;
-  for (;;) {
-    for (; blk < 2 * hi; ++blk) {
-      const int pg = blk >> 1, kb = blk & 1;
-      uint8_t* stage = kv_lds + ((pg - lo) & 1) * kPageBytes;
-      if (kb == 0 && blk != resumed) {
-        wait_vmem_all();  // this wave's copies of page pg have landed
-        __syncthreads();  // ... and everyone's; the other buffer is no longer read
-        if (pg + 1 < hi)
-          stage_page<NW>(a, so, kv_lds + (((pg + 1 - lo) & 1) * kPageBytes), b, pg + 1, L);
-      }
-      const int lim = n_vis - pg * kPage - kb * kBlockRows;
-      if (!attend_block(stage + kb * kBlockRows * kRowBytes, rb, qreg, ws, lim, a.scale_log2))
-        break;
-    }
-    if (blk >= 2 * hi) break;
-    apply_rescale(ws);
-    resumed = blk;
-  }
-  __syncthreads();  // both buffers free before the next piece stages into them
+  f32x4* xs = xbuf + wave * 4 * 64;
+  const int partner_off = (c ? -4 : 4) * 64;
+  int bt_first = lo;
+  fill_bt_cache(a, bt_cache, b, bt_first, hi);
+  // the query loads above must not be awaited inside the block loop, where the next
+  // stages' copies are in flight: settle every outstanding load once here
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // ---- epilogue: normalise; final result or partial for the combine pass
-  const float l_tot = row_sum(ws.l_run);
-  const float l_bf = row_sum(ws.l_bf);
-  const bool seen = l_tot > 0.0f;
-  const float inv = (seen && l_bf > 0.0f) ? 1.0f / l_bf : 0.0f;
-  const float lse2 = seen ? ws.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-  float inv_i[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) inv_i[i] = __shfl(inv, acc_row(lane, i), 64);
-
-  float* obase = whole ? a.O + ((size_t)b * M + m_wave) * kNope
-                       : a.part_o + ((size_t)slot * a.slot_rows + (m_wave - mt * MT)) * kNope;
-  const int dcol = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = acc_row(lane, i);
-    if (m_wave + r < M) {
-      float* orow = obase + (size_t)r * kNope + dcol;
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) orow[db * 16] = ws.acc[db][i] * inv_i[i];
+  // issue block i into ring slot i % kStages (refilling the block-table cache when
+  // the block's page leaves it; that refill is workgroup-uniform and ends in a barrier)
+  auto issue = [&](int i) {
+    const int pg = lo + (i >> 1), half = i & 1;
+    if (pg - bt_first >= kBtCache || pg < bt_first) {
+      bt_first = pg;
+      fill_bt_cache(a, bt_cache, b, bt_first, hi);
     }
+    const int valid = min(kKvBlock, L - pg * kPage - half * kKvBlock);
+    stage_half(a.kv_pool, so, ring + (i % kStages) * kStageBytes, bt_cache[pg - bt_first], half,
+               valid);
+  };
+
+  // At most two passes: the second (rare) one starts from the rows' true maxima.
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int ct = 0; ct < kColTilesPerWave; ++ct) ws.acc[ct] = f32x16{};
+    ws.m_ref = pass == 0 ? -INFINITY : ws.m_seen;
+    ws.l_run = 0.0f;
+    ws.l_bf = 0.0f;
+    if (nb > 0) issue(0);
+    if (nb > 1) issue(1);
+    for (int i = 0; i < nb; ++i) {
+      // this wave's copies of block i have landed (block i + 1 may still be in flight)
+      if (i + 1 < nb)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageCopiesPerWave) : "memory");
+      else
+        wait_vmem_all();
+      __syncthreads();  // ... everyone's; and every wave is done with block i - 1's slot
+      if (i + 2 < nb) issue(i + 2);
+      const int pg = lo + (i >> 1), half = i & 1;
+      const int lim = n_vis - pg * kPage - half * kKvBlock;
+      attend_block(ring + (i % kStages) * kStageBytes, rb, qreg, xs, partner_off, ws, lim,
+                   a.scale_log2);
+    }
+    // a row whose scores outgrew its reference by more than the lazy bound forces a
+    // second pass for the whole workgroup
+    const bool broke = ws.m_ref != -INFINITY && ws.m_seen > ws.m_ref + kLazyRescale;
+    if (threadIdx.x == 0) *redo_flag = 0;
+    __syncthreads();  // every wave is done with the ring and the exchange slots
+    if (__builtin_amdgcn_ballot_w64(broke) && lane == 0) *redo_flag = 1;
+    __syncthreads();
+    const bool redo = *redo_flag != 0;
+    __syncthreads();  // the flag has been read before anyone resets it
+    if (!redo) break;
   }
-  if (lane < 16 && q_ok) {
-    if (whole)
-      a.lse[(size_t)b * M + m_q] = lse2 * 0.69314718055994531f;
-    else
-      a.part_lse[(size_t)slot * a.slot_rows + (m_q - mt * MT)] = lse2;
-  }
+
+  write_rows(a, ws, pair32_sum(ws.l_run), pair32_sum(ws.l_bf), b, m_slice, p * kRowsPerWave, c,
+             whole, slot);
 }
 
-template <int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 splitkv_kernel(SplitArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2 * kPageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
+  __shared__ f32x4 xbuf[kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
   __shared__ int prefix[kMaxBatch + 1];
+  __shared__ int bt_cache[kBtCache];
+  __shared__ int redo_flag;
 
   const int lam = xcd_logical_id(blockIdx.x, gridDim.x);
   const int g = lam / a.n_mt;
@@ -396,21 +448,51 @@ splitkv_kernel(SplitArgs a) {
     const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
     const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
     const bool whole = plo == 0 && phi == pb1 - pb0;
-    run_piece<NW>(a, kv_lds, __builtin_amdgcn_readfirstlane(b), mt,
-                  __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi), whole,
-                  (b + g) * a.n_mt + mt);
+    run_piece(a, ring, xbuf, bt_cache, &redo_flag, __builtin_amdgcn_readfirstlane(b), mt,
+              __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi), whole,
+              (b + g) * a.n_mt + mt);
+    __syncthreads();  // LDS free before the next piece stages into it
   }
 }
 
-// One wave per folded query row of a split request: LSE-weighted sum of partials.
+// ---- combine ---------------------------------------------------------------------
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) r += red[w];
+  return r;
+}
+
+// One workgroup per folded query row (b, m) of a split request.  Thread t handles
+// columns 8 (t % 64) .. + 8 of every fourth piece starting at t / 64; the four
+// piece lanes are summed through LDS.
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
   __shared__ int prefix[kMaxBatch + 1];
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ __attribute__((aligned(16))) float part[kCombineThreads / 64][64 * 8];
   build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, false);
   const int64_t T = prefix[a.B];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t gr = (int64_t)blockIdx.x * (kCombineThreads / 64) + wave;
-  if (gr >= (int64_t)a.B * a.M) return;
-  const int b = (int)(gr / a.M), m = (int)(gr - (int64_t)b * a.M);
+  const int row = blockIdx.x;
+  const int b = row / a.M, m = row - b * a.M;
   const int pb0 = prefix[b], pb1 = prefix[b + 1];
   if (pb1 <= pb0) return;
   const int g0 = part_of(T, a.G, pb0);
@@ -426,76 +508,79 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
     const size_t slot = (size_t)(b + g) * a.n_mt + mt;
     return a.part_lse[slot * a.slot_rows + ml];
   };
+  const int tid = threadIdx.x;
   float mx = -INFINITY;
-  for (int s = lane; s < n; s += 64) mx = fmaxf(mx, lse_of(s));
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+  for (int s = tid; s < n; s += kCombineThreads) mx = fmaxf(mx, lse_of(s));
+  mx = block_max(mx, red);
   float tot = 0.0f;
   if (mx != -INFINITY)
-    for (int s = lane; s < n; s += 64) tot += exp2f(lse_of(s) - mx);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) tot += __shfl_xor(tot, d, 64);
+    for (int s = tid; s < n; s += kCombineThreads) tot += exp2f(lse_of(s) - mx);
+  tot = block_sum(tot, red);
   const bool seen = tot > 0.0f;
   const float lse2 = seen ? mx + log2f(tot) : -INFINITY;
 
+  const int cg = tid & 63, pl = tid >> 6;
+  constexpr int kLanes = kCombineThreads / 64;
   f32x4 o0 = {}, o1 = {};
-  const int d0 = lane * 8;
-  constexpr int U = 8;
-  int s = 0;
-  for (; s + U <= n; s += U) {
+  constexpr int U = 4;
+  int s = pl;
+  for (; s + kLanes * (U - 1) < n; s += kLanes * U) {
     f32x4 v0[U], v1[U];
     float w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t slot = (size_t)(b + g0 + s + u) * a.n_mt + mt;
-      const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + d0;
+      const int su = s + kLanes * u;
+      const size_t slot = (size_t)(b + g0 + su) * a.n_mt + mt;
+      const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * cg;
       v0[u] = *reinterpret_cast<const f32x4*>(src);
       v1[u] = *reinterpret_cast<const f32x4*>(src + 4);
-      const float l = lse_of(s + u);
+      const float l = lse_of(su);
       w[u] = (seen && l != -INFINITY) ? exp2f(l - lse2) : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (w[u] != 0.0f) {  // a zero-weight slot may hold stale data, even NaN
-        o0 += w[u] * v0[u];
-        o1 += w[u] * v1[u];
-      }
+      // a zero-weight slot may hold stale data, even NaN: select, never multiply
+      o0 = w[u] != 0.0f ? o0 + w[u] * v0[u] : o0;
+      o1 = w[u] != 0.0f ? o1 + w[u] * v1[u] : o1;
     }
   }
-  for (; s < n; ++s) {
+  for (; s < n; s += kLanes) {
     const float l = lse_of(s);
     const float w = (seen && l != -INFINITY) ? exp2f(l - lse2) : 0.0f;
     if (w != 0.0f) {
       const size_t slot = (size_t)(b + g0 + s) * a.n_mt + mt;
-      const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + d0;
+      const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * cg;
       o0 += w * *reinterpret_cast<const f32x4*>(src);
       o1 += w * *reinterpret_cast<const f32x4*>(src + 4);
     }
   }
-  float* dst = a.O + ((size_t)b * a.M + m) * kNope + d0;
-  *reinterpret_cast<f32x4*>(dst) = o0;
-  *reinterpret_cast<f32x4*>(dst + 4) = o1;
-  if (lane == 0) a.lse[(size_t)b * a.M + m] = lse2 * 0.69314718055994531f;
+  *reinterpret_cast<f32x4*>(&part[pl][8 * cg]) = o0;
+  *reinterpret_cast<f32x4*>(&part[pl][8 * cg + 4]) = o1;
+  __syncthreads();
+  if (pl == 0) {
+#pragma unroll
+    for (int p = 1; p < kLanes; ++p) {
+      o0 += *reinterpret_cast<const f32x4*>(&part[p][8 * cg]);
+      o1 += *reinterpret_cast<const f32x4*>(&part[p][8 * cg + 4]);
+    }
+    float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * cg;
+    *reinterpret_cast<f32x4*>(dst) = o0;
+    *reinterpret_cast<f32x4*>(dst + 4) = o1;
+    if (cg == 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
+  }
 }
 
-hipError_t launch_splitkv(const SplitArgs& a, int waves, hipStream_t stream) {
+hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.G * a.n_mt;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  if (waves == 8)
-    hipLaunchKernelGGL(splitkv_kernel<8>, dim3((unsigned)nwg), dim3(64 * 8), 0, stream, a);
-  else if (waves == 4)
-    hipLaunchKernelGGL(splitkv_kernel<4>, dim3((unsigned)nwg), dim3(64 * 4), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(splitkv_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.M;
-  const int64_t per = kCombineThreads / 64;
-  const int64_t nwg = (rows + per - 1) / per;
-  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)nwg), dim3(kCombineThreads), 0, stream, a);
+  if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 
