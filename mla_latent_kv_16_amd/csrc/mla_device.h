@@ -87,7 +87,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // *other* stage buffer to these copies (it would wait for every copy in flight);
 // completion is awaited explicitly with wait_vmem_all() before the barrier that
 // publishes a stage.  The kernels use no M0-relative instructions of their own.
-__device__ __forceinline__ void dma16(const void* sbase, int voff, uint32_t lds) {
+// Both are passed through readfirstlane so that they are scalar operands even where
+// the compiler cannot prove them uniform.
+__device__ __forceinline__ void dma16(const void* sbase_in, int voff, uint32_t lds_in) {
+  const uint64_t p = reinterpret_cast<uint64_t>(sbase_in);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  const void* sbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds)

@@ -160,7 +160,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* blk, const ReadBases
                                              WaveState& ws, int lim, float scale_log2) {
   const int lane = threadIdx.x & 63;
   constexpr int DQ = 4;                      // A-operand reads in flight
-  constexpr int DV = 2;                      // V-operand read pairs in flight
+  constexpr int DV = 4;                      // V-operand read pairs in flight
   constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
 
   const uint8_t* kbase[4];
@@ -178,17 +178,22 @@ __device__ __forceinline__ void attend_block(const uint8_t* blk, const ReadBases
     return lds_read_tr(vbase[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
   };
 
-  // ---- S^T = K Q^T over this wave's half of the 576-wide rows
-  f32x16 s = {};
+  // ---- S^T = K Q^T over this wave's half of the 576-wide rows, in two accumulation
+  // chains (even / odd k-steps)
+  f32x16 s = {}, s1 = {};
   bf16x8 abuf[DQ];
 #pragma unroll
   for (int u = 0; u < DQ; ++u) abuf[u] = qk_read(u);
 #pragma unroll
   for (int kk = 0; kk < kQStepsPerWave; ++kk) {
-    s = mfma32(abuf[kk % DQ], qreg[kk], s);
+    if (kk & 1)
+      s1 = mfma32(abuf[kk % DQ], qreg[kk], s1);
+    else
+      s = mfma32(abuf[kk % DQ], qreg[kk], s);
     if (kk + DQ < kQStepsPerWave) abuf[kk % DQ] = qk_read(kk + DQ);
     __builtin_amdgcn_sched_barrier(0);
   }
+  s += s1;
 
   // ---- exchange the halves: own + partner is the same sum on both waves
 #pragma unroll
