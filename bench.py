@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the paged latent-KV MLA decode hot path on one MI355X.
 
-One step is one full decode call: the split-KV attention pass plus the
-log-sum-exp combine pass over one batch, with every input already resident in
-HBM.  The default workload is speculative-verify decode at B=4, Sq=4 draft
-tokens, H=16 heads (one GPU's share of a 64-head model at attention TP4) over a
-65,536-token cached prefix per request (spec4).  Inputs are seeded synthetic
-tensors shaped like the pages' coding-agent workloads.
+One step is one full decode call over one batch: the split-KV attention pass plus
+the log-sum-exp combine pass, with every input already resident in HBM.  The
+default workload is speculative-verify decode at B=4, Sq=4 draft tokens, H=16
+heads (one GPU's share of a 64-head model at attention TP4) over a 65,536-token
+cached prefix per request ("spec4").  Inputs are seeded synthetic tensors shaped
+like the pages' coding-agent workloads.
 
-Prints one JSON line.  `value` is KV-read throughput: latent bytes the step must
+Prints one JSON line.  `value` is KV-read throughput: the latent bytes a step must
 read (every visible row once, 576 bf16) divided by the measured time per step.
-`roofline` rates the dominant kernel (the split-KV pass) against MI355X HBM peak
-using per-launch HIP events recorded on the stream the kernels run on.
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+`roofline` rates the dominant kernel (the split-KV pass) against its MI355X peak,
+with per-launch HIP events recorded on the stream the kernels run on; its
+`traffic` is the HBM bytes per launch measured by rocprofv3 counters (stored under
+profiles/ and used only while the kernel sources are unchanged).  `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -27,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "MLA decode µs/step + KV-read HBM GB/s (% peak), B=4/8/16, Sq=4–16, 64K ctx"
 
 
 def log(*a):
@@ -34,7 +37,12 @@ def log(*a):
 
 
 def algorithmic_work(w):
-    """Bytes a step must move and flops it must do (split partials not counted)."""
+    """Bytes a step must move and flops it must do (split partials not counted).
+
+    Bytes: every visible latent row once (576 bf16), the queries (576 bf16 per
+    folded row), the outputs (512 fp32 + 1 fp32 LSE per folded row) and the block
+    table entries of the visible pages.  Flops: 2 (576 + 512) per visible
+    (query row, key) pair."""
     import numpy as np
     L = w.seq_lens.astype(np.int64)
     M = w.Sq * w.H
@@ -43,18 +51,18 @@ def algorithmic_work(w):
     q = w.B * M * 1152
     out = w.B * M * (512 * 4 + 4)
     bt = pages * 4
-    flops = 0
-    for b in range(w.B):
-        for t in range(w.Sq):
-            n_vis = int(L[b]) - w.Sq + t + 1 if w.causal else int(L[b])
-            flops += w.H * n_vis * 2 * (576 + 512)
+    t = np.arange(w.Sq, dtype=np.int64)
+    if w.causal:
+        n_vis = (L[:, None] - w.Sq + t[None, :] + 1).sum()
+    else:
+        n_vis = L.sum() * w.Sq
+    flops = int(n_vis) * w.H * 2 * (576 + 512)
     return dict(kv_bytes=kv, bytes=kv + q + out + bt, flops=flops, pages=pages)
 
 
 def cpu_baseline(w, budget_s=12.0):
     """fp64 oracle on whole requests (cycling through the batch) until ~budget_s has
     passed; KV bytes of the requests done over the wall time, in GB/s."""
-    import numpy as np
     from oracle import mla_attention_folded
     try:
         from threadpoolctl import threadpool_info
@@ -78,6 +86,23 @@ def cpu_baseline(w, budget_s=12.0):
             "seconds_per_step_extrapolated": dt * w.B / done}
 
 
+def stored_traffic(config):
+    """HBM bytes per split-KV launch from profiles/traffic_<config>.json, if the
+    counters were taken on the current kernel sources."""
+    from mla_latent_kv_16_amd.profiling import kernel_hash
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    fb, wb = rec.get("split_fetch_bytes"), rec.get("split_write_bytes")
+    if fb is None or wb is None:
+        return None
+    return int(fb + wb)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +114,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies cycled per step (0 = enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, launch a plain 256 MiB device copy 3 times (counter "
+                         "calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -119,8 +147,6 @@ def main():
     pools = [t(w.kv_pool) for _ in range(n_copies)]
     bt = torch.from_numpy(w.block_table).to(dev)
     sl = torch.from_numpy(w.seq_lens).to(dev)
-    M = w.Sq * w.H
-    is_prefill = args.config == "prefill"
     G = args.partitions or mla.auto_partitions(w.B, w.Sq, w.H, w.max_pages)
     ws = mla.new_workspace(w.B, w.Sq, w.H, w.max_pages, G, device=dev)
     O = torch.empty((w.B, w.Sq, w.H, 512), dtype=torch.float32, device=dev)
@@ -144,6 +170,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # The library launches on torch's current stream, where these events are recorded.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -158,19 +185,31 @@ def main():
     if mla.read_error_flags(ws):
         raise SystemExit("kernel reported a data fault flag")
 
+    if args.copy_probe:
+        from mla_latent_kv_16_amd.profiling import COPY_PROBE_BYTES
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     value = work["kv_bytes"] / (ms_step * 1e-3) / 1e9
-    if is_prefill:
-        achieved = work["flops"] / (split_avg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None}
+    hbm_achieved = work["bytes"] / (split_avg * 1e-3) / 1e9
+    mfma_achieved = work["flops"] / (split_avg * 1e-3) / 1e12
+    traffic = stored_traffic(args.config)
+    mfma_bound = args.config in ("prefill", "spec16")
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(mfma_achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
-        achieved = work["bytes"] / (split_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+        roof = {"bound": "hbm", "achieved": round(hbm_achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic}
     log(f"step {ms_step * 1e3:.1f} us (split pass {split_avg * 1e3:.1f} us, "
         f"p10 {np.percentile(split_ms, 10) * 1e3:.1f} p90 {np.percentile(split_ms, 90) * 1e3:.1f}); "
-        f"{value:.0f} GB/s of KV; {work['flops'] / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s")
+        f"{value:.0f} GB/s of KV; split pass {hbm_achieved:.0f} GB/s, {mfma_achieved:.1f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -180,7 +219,7 @@ def main():
         log(f"cpu oracle: {cpu['value']:.4f} GB/s on {cpu['cores']} threads ({cpu['sample']})")
 
     line = {
-        "metric": "MLA decode µs/step + KV-read HBM GB/s (% peak), B=4/8/16, Sq=4–16, 64K ctx",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -198,6 +237,9 @@ def main():
                    "page_size": 64, "latent": "512+64 bf16", "partitions": G,
                    "kv_bytes": work["kv_bytes"], "tflops_per_step": work["flops"] / 1e12},
         "kv_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "split_pass_us": round(split_avg * 1e3, 2),
+        "split_pass_hbm_frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
+        "split_pass_mfma_frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

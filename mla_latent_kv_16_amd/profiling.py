@@ -1,0 +1,134 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m mla_latent_kv_16_amd.profiling stats   <kernel_stats.csv> <out.md> "<command>"
+    python -m mla_latent_kv_16_amd.profiling traffic <fetch_counter.csv> <write_counter.csv>
+                                                     <workload> <out.json> "<commands>"
+
+`stats` keeps the per-kernel table of a `--kernel-trace --stats` run.  `traffic`
+turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of `bench.py --copy-probe`
+into HBM bytes per launch of the split-KV kernel: each counter is scaled by what the
+same counter reads for the plain device copy of known size that `--copy-probe`
+launches, and the result is stamped with a hash of the kernel sources so that
+bench.py reports it only while the kernel is unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["csrc/mla_kernels.hip", "csrc/mla_device.h", "csrc/mla_internal.h",
+                  "csrc/mla_api.hip"]
+SPLIT_KERNEL = "splitkv_kernel"
+COMBINE_KERNEL = "combine_kernel"
+# bench.py --copy-probe copies this many bytes per launch (a plain device-to-device copy)
+COPY_PROBE_BYTES = 256 << 20
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def stats_table(path: str) -> str:
+    rows = _rows(path)
+    out = ["| kernel | calls | total (us) | average (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KERNEL_NAME") or r.get("Kernel_Name")
+        calls = int(float(r.get("Calls", 0)))
+        tot = float(r.get("TotalDurationNs", 0)) / 1e3
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        mn = float(r.get("MinNs", 0)) / 1e3
+        mx = float(r.get("MaxNs", 0)) / 1e3
+        pct = float(r.get("Percentage", 0))
+        out.append(f"| `{name[:90]}` | {calls} | {tot:.1f} | {avg:.2f} | {mn:.2f} | {mx:.2f} | "
+                   f"{pct:.1f}% |")
+    return "\n".join(out)
+
+
+def counter_per_kernel(path: str, counter: str):
+    """{kernel name: [per-dispatch values]} for one counter of a --pmc CSV."""
+    acc = defaultdict(list)
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return acc
+
+
+def _pick(acc, needle):
+    vals = [v for k, vs in acc.items() if needle in k for v in vs]
+    return sum(vals) / len(vals) if vals else None
+
+
+def _copy_value(acc):
+    """Per-dispatch counter value of the copy probe: the copy kernels that moved
+    COPY_PROBE_BYTES (the largest dispatches of any copy-like kernel)."""
+    cands = []
+    for k, vs in acc.items():
+        low = k.lower()
+        if "copy" in low or "elementwise" in low:
+            cands.extend(vs)
+    if not cands:
+        return None
+    top = max(cands)
+    big = [v for v in cands if v > 0.5 * top]
+    return sum(big) / len(big)
+
+
+def traffic(fetch_csv: str, write_csv: str, workload: str, commands: str) -> dict:
+    f_acc = counter_per_kernel(fetch_csv, "FETCH_SIZE")
+    w_acc = counter_per_kernel(write_csv, "WRITE_SIZE")
+    kib_copy = COPY_PROBE_BYTES / 1024.0
+    f_copy = _copy_value(f_acc)
+    w_copy = _copy_value(w_acc)
+    f_scale = kib_copy / f_copy if f_copy else None
+    w_scale = kib_copy / w_copy if w_copy else None
+    res = {"workload": workload, "kernel_hash": kernel_hash(), "commands": commands,
+           "copy_probe_bytes": COPY_PROBE_BYTES,
+           "fetch_kib_copy_probe": f_copy, "write_kib_copy_probe": w_copy,
+           "fetch_scale": f_scale, "write_scale": w_scale}
+    for tag, needle in (("split", SPLIT_KERNEL), ("combine", COMBINE_KERNEL)):
+        fk = _pick(f_acc, needle)
+        wk = _pick(w_acc, needle)
+        res[f"{tag}_fetch_kib_raw"] = fk
+        res[f"{tag}_write_kib_raw"] = wk
+        res[f"{tag}_fetch_bytes"] = fk * 1024 * f_scale if fk is not None and f_scale else None
+        res[f"{tag}_write_bytes"] = wk * 1024 * w_scale if wk is not None and w_scale else None
+    return res
+
+
+def main(argv):
+    if len(argv) >= 4 and argv[0] == "stats":
+        src, dst, cmd = argv[1], argv[2], argv[3]
+        with open(dst, "w") as f:
+            f.write(f"# Kernel trace summary\n\nCommand:\n\n```\n{cmd}\n```\n\n")
+            f.write(f"Kernel sources hash: `{kernel_hash()}`\n\n")
+            f.write(stats_table(src) + "\n")
+        print(dst)
+    elif len(argv) >= 6 and argv[0] == "traffic":
+        res = traffic(argv[1], argv[2], argv[3], argv[5])
+        with open(argv[4], "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res, indent=1))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
