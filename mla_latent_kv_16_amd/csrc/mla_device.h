@@ -33,12 +33,13 @@ constexpr int kKvBlock = 32;                       // kv rows per MFMA block (S^
 constexpr int kQStepsPerWave = kRow / 16 / 2;      // 18 MFMA k-steps: half the 576-wide row
 constexpr int kColTilesPerWave = kNope / 32 / 2;   // 8 output column tiles of 32
 constexpr int kStageBytes = kKvBlock * kRowBytes;  // 36,864: half a page
-constexpr int kStages = 3;                         // LDS ring depth (two blocks in flight)
-constexpr int kStageCopiesPerWave = 9;             // 16-byte-per-lane copies per wave per stage
+constexpr int kStages = 3;                         // LDS ring depth
+constexpr int kStageCopiesPerWave = 9;             // 16-byte-per-lane copies per wave per block
 constexpr int kCombineThreads = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -84,12 +85,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Direct global -> LDS copy of 16 bytes per lane: lane l reads sbase + voff and
 // writes LDS bytes [lds + 16 l, lds + 16 l + 16).  sbase and lds are wave-uniform.
 // Issued as inline asm so that the compiler does not tie later LDS reads of the
-// *other* stage buffer to these copies (it would wait for every copy in flight);
+// *other* ring slots to these copies (it would wait for every copy in flight);
 // completion is awaited explicitly with wait_vmem_all() before the barrier that
-// publishes a stage.  The kernels use no M0-relative instructions of their own.
-// Both are passed through readfirstlane so that they are scalar operands even where
-// the compiler cannot prove them uniform.
-__device__ __forceinline__ void dma16(const void* sbase_in, int voff, uint32_t lds_in) {
+// publishes a slot.  M0 is reserved to the compiler, which on gfx9 and later sets
+// it only for instructions these kernels do not use (LDS-DMA builtins, message
+// sends, indirect register indexing), so the asm may overwrite it.  Both are passed through readfirstlane (as unsigned 32-bit
+// halves) so that they are scalar operands even where the compiler cannot prove
+// them uniform.
+__device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
   const uint64_t p = reinterpret_cast<uint64_t>(sbase_in);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));

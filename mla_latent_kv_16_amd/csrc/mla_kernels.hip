@@ -56,51 +56,50 @@ __device__ __forceinline__ int acc_row(int lane, int i) {
   return 4 * (lane >> 5) + 8 * (i >> 2) + (i & 3);
 }
 
-// ---- staging a half page into LDS -----------------------------------------------
-// A stage is 32 rows = 4 groups of 8 rows; wave w copies group w: 576 sixteen-byte
-// chunks, i.e. 9 copies of 64 lanes x 16 bytes.  LDS chunk position q of the group
-// receives the global chunk the swizzled layout wants there; the swizzle of a row
-// depends only on its index mod 16, so the half of the page does not matter.
-// Rows at or past `valid` re-read the stage's last valid row (finite data whose
-// scores are masked), so nothing past the request's length is touched.
+// ---- staging a block into LDS ----------------------------------------------------
+// A block is 32 rows (half a page) = 4 groups of 8 rows; wave w copies group w:
+// 576 sixteen-byte chunks, i.e. 9 direct global->LDS copies of 64 lanes x 16 bytes.
+// LDS chunk position q of the group receives the global chunk the swizzled layout
+// wants there; the swizzle of a row depends only on its index mod 16, so the half
+// of the page does not matter.  Rows at or past `valid` re-read the block's last
+// valid row (finite data whose scores are masked), so nothing past the request's
+// length is touched.
 struct StageOffsets {
-  int off[kStageCopiesPerWave];  // per-lane source offset of copy i, rows 8 w .. 8 w + 7
+  uint32_t off[kStageCopiesPerWave];  // per-lane source offset of copy i (rows 8 w .. 8 w + 7)
 };
 
 __device__ __forceinline__ StageOffsets stage_offsets() {
   StageOffsets so;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < kStageCopiesPerWave; ++i) {
-    const int q = i * 64 + lane;
-    const int rr = q / kChunks;
-    const int pos = q - rr * kChunks;
-    const int r = 8 * wave + rr;
+    const uint32_t q = i * 64 + lane;
+    const uint32_t rr = q / kChunks;
+    const uint32_t pos = q - rr * kChunks;
+    const uint32_t r = 8 * wave + rr;
     so.off[i] = r * kRowBytes + ((pos ^ swz(r)) << 4);
   }
   return so;
 }
 
-__device__ __forceinline__ void stage_half(const uint16_t* kv_pool, const StageOffsets& so,
-                                           uint8_t* stage, int phys, int half, int valid) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  phys = __builtin_amdgcn_readfirstlane(phys);
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(kv_pool) + (size_t)phys * kPageBytes +
-                       half * kStageBytes;
-  const int row0 = 8 * wave;
-  const uint32_t dst = lds_addr(stage) + row0 * kRowBytes;
-  if (row0 + 8 <= valid) {
+// Copies this wave's share of the block whose first row is at `src` (wave-uniform)
+// into ring slot `slot`.
+__device__ __forceinline__ void stage_block(const uint8_t* src, uint8_t* slot, int valid,
+                                            const StageOffsets& so) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t dst = lds_addr(slot) + 8 * wave * kRowBytes;
+  if (8 * (int)wave + 8 <= valid) {
 #pragma unroll
     for (int i = 0; i < kStageCopiesPerWave; ++i) dma16(src, so.off[i], dst + i * 1024);
-  } else {
+  } else {  // the request's last block: rows past its length re-read row valid - 1
 #pragma unroll
     for (int i = 0; i < kStageCopiesPerWave; ++i) {
-      const int q = i * 64 + lane;
-      const int rr = q / kChunks;
-      const int pos = q - rr * kChunks;
-      const int r = row0 + rr;
-      const int rs = min(r, valid - 1);
+      const uint32_t q = i * 64 + lane;
+      const uint32_t rr = q / kChunks;
+      const uint32_t pos = q - rr * kChunks;
+      const uint32_t r = 8 * wave + rr;
+      const uint32_t rs = min(r, (uint32_t)(valid - 1));
       dma16(src, rs * kRowBytes + ((pos ^ swz(r)) << 4), dst + i * 1024);
     }
   }
@@ -144,121 +143,151 @@ __device__ __forceinline__ ReadBases read_bases(int c) {
   return rb;
 }
 
-// One block of 32 kv rows (stage `blk` in LDS) against this wave pair's 32 query
-// rows.  Each wave of the pair computes S^T = K Q^T over its half of the contraction,
-// the halves are exchanged through `xs` (this wave's slot; the partner's is the
-// neighbouring one), then both waves run the same softmax step on the full scores
-// and accumulate O += P V for their 256 columns.  `lim` is the number of leading
-// rows of the block this lane's query row may see.  Contains one workgroup
-// barrier: every wave of the workgroup must call it for the same blocks.
+// ---- the software pipeline --------------------------------------------------------
+// Iteration i of a piece runs the softmax step and O += P V of block i while the MFMA
+// pipe computes this wave's half of S^T = K Q^T for block i + 1.  A wave pair owns 32
+// query rows: each wave scores half of the 576-wide contraction, the halves of a
+// block's S^T are swapped through LDS across the iteration barrier, and each wave
+// accumulates O for its 256 of the 512 output columns.
 //
 // LDS operand reads run a fixed distance ahead of the MFMAs that consume them and
-// sched_barrier pins that order, so the compiler neither serialises each read with
-// its MFMA nor hoists every read (and its registers) to the top.
-__device__ __forceinline__ void attend_block(const uint8_t* blk, const ReadBases& rb,
-                                             const bf16x8* qreg, f32x4* xs, int partner_off,
-                                             WaveState& ws, int lim, float scale_log2) {
-  const int lane = threadIdx.x & 63;
-  constexpr int DQ = 4;                      // A-operand reads in flight
-  constexpr int DV = 4;                      // V-operand read pairs in flight
-  constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
+// sched_barrier pins the order of the interleaved MFMA, VALU and LDS work, so the
+// compiler neither serialises each read with its MFMA nor hoists everything to the top.
 
-  const uint8_t* kbase[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) kbase[j] = blk + rb.k[j];
-  const uint8_t* vbase[2][2];
-#pragma unroll
-  for (int sd = 0; sd < 2; ++sd)
-#pragma unroll
-    for (int par = 0; par < 2; ++par) vbase[sd][par] = blk + rb.v[sd][par];
-  auto qk_read = [&](int kk) { return lds_read_b128(kbase[kk & 3], (kk >> 2) * 128); };
-  // t = 8 ks + ct, ks-major so consecutive MFMAs use different accumulators
-  auto pv_read = [&](int t, int sd) {
-    const int ks = t >> 3, ct = t & 7;
-    return lds_read_tr(vbase[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
-  };
-
-  // ---- S^T = K Q^T over this wave's half of the 576-wide rows, in two accumulation
-  // chains (even / odd k-steps)
-  f32x16 s = {}, s1 = {};
+// Own half of S^T for one staged block (the pipeline's first block).
+__device__ __forceinline__ f32x16 qk_partial(const uint8_t* blk, const ReadBases& rb,
+                                             const bf16x8* qreg) {
+  constexpr int DQ = 4;
+  auto qk_read = [&](int kk) { return lds_read_b128(blk + rb.k[kk & 3], (kk >> 2) * 128); };
+  f32x16 s0 = {};
   bf16x8 abuf[DQ];
 #pragma unroll
   for (int u = 0; u < DQ; ++u) abuf[u] = qk_read(u);
 #pragma unroll
   for (int kk = 0; kk < kQStepsPerWave; ++kk) {
-    if (kk & 1)
-      s1 = mfma32(abuf[kk % DQ], qreg[kk], s1);
-    else
-      s = mfma32(abuf[kk % DQ], qreg[kk], s);
+    s0 = mfma32(abuf[kk % DQ], qreg[kk], s0);
     if (kk + DQ < kQStepsPerWave) abuf[kk % DQ] = qk_read(kk + DQ);
     __builtin_amdgcn_sched_barrier(0);
   }
-  s += s1;
+  return s0;
+}
 
-  // ---- exchange the halves: own + partner is the same sum on both waves
+__device__ __forceinline__ void store_partial(f32x4* xs, const f32x16& s) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     xs[j * 64 + lane] = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
-  __syncthreads();
+}
+
+// One iteration.  `own` and `partner` are the two halves of block i's S^T in LDS
+// (this wave's and the other wave's of the pair); xs_next receives this wave's half
+// of block i + 1 (when HAS_NEXT).  `lim` is the number of leading rows of block i
+// this lane's query row may see.
+template <bool HAS_NEXT>
+__device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk_next,
+                                          const ReadBases& rb, const bf16x8* qreg,
+                                          const f32x4* own, const f32x4* partner, f32x4* xs_next,
+                                          WaveState& ws, int lim, float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  constexpr int DQ = 4;                      // A-operand reads in flight
+  constexpr int DV = 4;                      // V-operand read pairs in flight
+  constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
+  auto qk_read = [&](int kk) { return lds_read_b128(blk_next + rb.k[kk & 3], (kk >> 2) * 128); };
+  // t = 8 ks + ct, ks-major so consecutive MFMAs use different accumulators
+  auto pv_read = [&](int t, int sd) {
+    const int ks = t >> 3, ct = t & 7;
+    return lds_read_tr(blk + rb.v[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
+  };
+
+  f32x4 ow[4], pr[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f32x4 o = xs[partner_off + j * 64 + lane];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s[4 * j + e] += o[e];
+    ow[j] = own[j * 64 + lane];
+    pr[j] = partner[j * 64 + lane];
   }
-
-  // first V operands go out before the softmax, which does not need them
-  bf16x4 vb0[DV], vb1[DV];
+  bf16x8 abuf[DQ];
+  if constexpr (HAS_NEXT) {
 #pragma unroll
-  for (int u = 0; u < DV; ++u) {
-    vb0[u] = pv_read(u, 0);
-    vb1[u] = pv_read(u, 1);
+    for (int u = 0; u < DQ; ++u) abuf[u] = qk_read(u);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- scale into the log2 domain, causal / length mask
-  f32x16 x = s * scale_log2;
-  if (__builtin_amdgcn_ballot_w64(lim < kKvBlock)) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (acc_row(lane, i) >= lim) x[i] = -INFINITY;
-  }
-
-  // ---- softmax step (a query row's 32 scores sit in lanes l and l + 32)
-  float mloc = x[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
-  mloc = pair32_max(mloc);
-  ws.m_seen = fmaxf(ws.m_seen, mloc);
-  if (ws.m_ref == -INFINITY) ws.m_ref = mloc;  // a row's first visible block sets it
-  const float m_use = (ws.m_ref == -INFINITY) ? 0.0f : ws.m_ref;
-  float psum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
-    psum += x[i];
-  }
-  ws.l_run += psum;
-
-  // P as the A operand of O = P V: for k-step ks lane holds query row lane % 32 and
-  // S^T registers 8 ks .. 8 ks + 7, i.e. kv rows 16 ks + 4 h + 0..3 and
-  // 16 ks + 8 + 4 h + 0..3; the V operand is read in that same kv-row order.  O is
-  // later divided by the sum of the rounded weights it was built from, so a row
-  // dominated by one key returns that key's c_kv up to fp32 rounding rather than
-  // up to bf16 rounding.
+  f32x16 x;
+  f32x16 n0 = {};
+  float m_use = 0.0f, psum = 0.0f;
   bf16x8 pa[2];
-  float pbf = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pa[ks][k] = static_cast<__bf16>(x[8 * ks + k]);
-      pbf += static_cast<float>(pa[ks][k]);
-    }
-  ws.l_bf += pbf;
-  __builtin_amdgcn_sched_barrier(0);
+  bf16x4 vb0[DV], vb1[DV];
 
-  // ---- O += P V, V = this wave's 256 c_kv columns of the same staged rows
+  // ---- S^T of block i + 1 on the MFMA pipe, the softmax step of block i in between
+#pragma unroll
+  for (int kk = 0; kk < kQStepsPerWave; ++kk) {
+    if constexpr (HAS_NEXT) {
+      n0 = mfma32(abuf[kk % DQ], qreg[kk], n0);
+      if (kk + DQ < kQStepsPerWave) abuf[kk % DQ] = qk_read(kk + DQ);
+    }
+    if (kk == 0) {
+      // full scores: own half + partner half (the same sum on both waves of the pair,
+      // fp32 addition being commutative); the log2-domain scale is applied below
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * j + e] = ow[j][e] + pr[j][e];
+    } else if (kk == 2) {
+      if (__builtin_amdgcn_ballot_w64(lim < kKvBlock)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (acc_row(lane, i) >= lim) x[i] = -INFINITY;
+      }
+    } else if (kk == 4) {
+      // row max (a query row's 32 scores sit in lanes l and l + 32), in the log2
+      // domain: scaling by a positive factor commutes with the max, rounding included
+      float mloc = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+      mloc = pair32_max(mloc) * scale_log2;
+      ws.m_seen = fmaxf(ws.m_seen, mloc);
+      if (ws.m_ref == -INFINITY) ws.m_ref = mloc;  // a row's first visible block sets it
+      m_use = (ws.m_ref == -INFINITY) ? 0.0f : ws.m_ref;
+    } else if (kk == 6 || kk == 8) {
+      const int i0 = kk == 6 ? 0 : 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i0 + i] = __builtin_amdgcn_exp2f(fmaf(x[i0 + i], scale_log2, -m_use));
+        psum += x[i0 + i];
+      }
+    } else if (kk == 10) {
+      // P as the A operand of O = P V: for k-step ks lane holds query row lane % 32 and
+      // S^T registers 8 ks .. 8 ks + 7, i.e. kv rows 16 ks + 4 h + 0..3 and
+      // 16 ks + 8 + 4 h + 0..3; the V operand is read in that same kv-row order.  O
+      // is later divided by the sum of the rounded weights it was built from, so a
+      // row dominated by one key returns that key's c_kv up to fp32 rounding rather
+      // than up to bf16 rounding.
+      ws.l_run += psum;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pa[ks][k] = static_cast<__bf16>(x[8 * ks + k]);
+      // sum of the rounded weights, two at a time (products with 1 are exact)
+      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      float pbf = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int k = 0; k < 8; k += 2)
+          pbf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pa[ks][k], pa[ks][k + 1]}, ones, pbf, false);
+      ws.l_bf += pbf;
+    } else if (kk == 12) {
+      // the first V operands of block i
+#pragma unroll
+      for (int u = 0; u < DV; ++u) {
+        vb0[u] = pv_read(u, 0);
+        vb1[u] = pv_read(u, 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- O += P V, V = this wave's 256 c_kv columns of block i, read transposed
 #pragma unroll
   for (int t = 0; t < NPV; ++t) {
     const int u = t % DV;
@@ -268,6 +297,9 @@ __device__ __forceinline__ void attend_block(const uint8_t* blk, const ReadBases
     if (t + DV < NPV) {
       vb0[u] = pv_read(t + DV, 0);
       vb1[u] = pv_read(t + DV, 1);
+    }
+    if constexpr (HAS_NEXT) {
+      if (t == 8) store_partial(xs_next, n0);  // block i + 1's half is complete
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -322,6 +354,36 @@ __device__ __forceinline__ void fill_bt_cache(const SplitArgs& a, int* bt_cache,
   __syncthreads();
 }
 
+// Ring slot of block i.  The byte offset is passed through an empty asm so that the
+// compiler keeps it a scalar added to a few per-lane bases, instead of strength-
+// reducing i % kStages into one loop-carried register per LDS read.
+__device__ __forceinline__ uint8_t* ring_slot(uint8_t* ring, int i) {
+  uint32_t off = (uint32_t)(i % kStages) * kStageBytes;
+  asm volatile("" : "+s"(off));
+  return ring + off;
+}
+
+// Loads this wave's share of block i of the piece (logical pages [lo, hi) of request
+// b, visible length L) into registers, refilling the block-table cache when the
+// block's page is not in it (workgroup-uniform, ends in a barrier).
+// Starts the copy of block i of the piece (logical page lo + i / 2, half i % 2) into
+// ring slot i % kStages.  Refilling the block-table cache is workgroup-uniform and
+// ends in a barrier.
+__device__ __forceinline__ void issue_block(const SplitArgs& a, uint8_t* ring,
+                                            const StageOffsets& so, int* bt_cache,
+                                            int& bt_first, int b, int lo, int hi, int L, int i) {
+  const int pg = lo + (i >> 1), half = i & 1;
+  if (pg - bt_first >= kBtCache || pg < bt_first) {
+    bt_first = pg;
+    fill_bt_cache(a, bt_cache, b, bt_first, hi);
+  }
+  const uint32_t phys = __builtin_amdgcn_readfirstlane(bt_cache[pg - bt_first]);
+  const int valid = min(kKvBlock, L - pg * kPage - half * kKvBlock);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_pool) +
+                       ((size_t)phys * kPageBytes + (size_t)half * kStageBytes);
+  stage_block(src, ring_slot(ring, i), valid, so);
+}
+
 // One piece: logical pages [lo, hi) of request b against M-tile mt.  The pages are
 // walked as 32-row blocks through a ring of kStages half-page stages, two blocks
 // ahead of the one being scored.
@@ -364,26 +426,11 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   ws.m_seen = -INFINITY;
   const ReadBases rb = read_bases(c);
   const StageOffsets so = stage_offsets();
-  f32x4* xs = xbuf + wave * 4 * 64;
-  const int partner_off = (c ? -4 : 4) * 64;
   int bt_first = lo;
   fill_bt_cache(a, bt_cache, b, bt_first, hi);
-  // the query loads above must not be awaited inside the block loop, where the next
-  // stages' copies are in flight: settle every outstanding load once here
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // issue block i into ring slot i % kStages (refilling the block-table cache when
-  // the block's page leaves it; that refill is workgroup-uniform and ends in a barrier)
-  auto issue = [&](int i) {
-    const int pg = lo + (i >> 1), half = i & 1;
-    if (pg - bt_first >= kBtCache || pg < bt_first) {
-      bt_first = pg;
-      fill_bt_cache(a, bt_cache, b, bt_first, hi);
-    }
-    const int valid = min(kKvBlock, L - pg * kPage - half * kKvBlock);
-    stage_half(a.kv_pool, so, ring + (i % kStages) * kStageBytes, bt_cache[pg - bt_first], half,
-               valid);
-  };
+  // xbuf holds two parities x four waves of S^T halves (4 x 64 lanes x f32x4 each)
+  auto xslot = [&](int parity, int w) { return xbuf + (parity * kWaves + w) * 4 * 64; };
 
   // At most two passes: the second (rare) one starts from the rows' true maxima.
   for (int pass = 0; pass < 2; ++pass) {
@@ -392,20 +439,34 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     ws.m_ref = pass == 0 ? -INFINITY : ws.m_seen;
     ws.l_run = 0.0f;
     ws.l_bf = 0.0f;
-    if (nb > 0) issue(0);
-    if (nb > 1) issue(1);
-    for (int i = 0; i < nb; ++i) {
-      // this wave's copies of block i have landed (block i + 1 may still be in flight)
-      if (i + 1 < nb)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageCopiesPerWave) : "memory");
-      else
-        wait_vmem_all();
-      __syncthreads();  // ... everyone's; and every wave is done with block i - 1's slot
-      if (i + 2 < nb) issue(i + 2);
-      const int pg = lo + (i >> 1), half = i & 1;
-      const int lim = n_vis - pg * kPage - half * kKvBlock;
-      attend_block(ring + (i % kStages) * kStageBytes, rb, qreg, xs, partner_off, ws, lim,
-                   a.scale_log2);
+    // Block j is copied into ring slot j % 3 from the start of iteration j - 2 (the
+    // slot's previous block, j - 3, was finished in iteration j - 3), its S^T halves
+    // are computed in iteration j - 1 and its softmax and P V run in iteration j.
+    // Prologue: blocks 0 and 1 in flight, S^T halves of block 0.
+    if (nb > 0) issue_block(a, ring, so, bt_cache, bt_first, b, lo, hi, L, 0);
+    if (nb > 1) issue_block(a, ring, so, bt_cache, bt_first, b, lo, hi, L, 1);
+    wait_vmem_all();
+    __syncthreads();  // blocks 0 and 1 are in LDS
+    if (nb > 0) store_partial(xslot(0, wave), qk_partial(ring_slot(ring, 0), rb, qreg));
+    // iteration i: wait for block i + 1, publish it and both S^T halves of block i,
+    // and start block i + 2 into the slot block i - 1 has left
+    auto top = [&](int i) {
+      wait_vmem_all();
+      __syncthreads();
+      if (i + 2 < nb) issue_block(a, ring, so, bt_cache, bt_first, b, lo, hi, L, i + 2);
+    };
+    auto lim_of = [&](int i) { return n_vis - (lo + (i >> 1)) * kPage - (i & 1) * kKvBlock; };
+    int i = 0;
+    for (; i + 1 < nb; ++i) {
+      top(i);
+      pipe_step<true>(ring_slot(ring, i), ring_slot(ring, i + 1), rb, qreg, xslot(i & 1, wave),
+                      xslot(i & 1, wave ^ 1), xslot((i + 1) & 1, wave), ws, lim_of(i),
+                      a.scale_log2);
+    }
+    if (i < nb) {
+      top(i);
+      pipe_step<false>(ring_slot(ring, i), nullptr, rb, qreg, xslot(i & 1, wave),
+                       xslot(i & 1, wave ^ 1), nullptr, ws, lim_of(i), a.scale_log2);
     }
     // a row whose scores outgrew its reference by more than the lazy bound forces a
     // second pass for the whole workgroup
@@ -426,7 +487,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 splitkv_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
-  __shared__ f32x4 xbuf[kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
+  __shared__ f32x4 xbuf[2 * kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
   __shared__ int prefix[kMaxBatch + 1];
   __shared__ int bt_cache[kBtCache];
   __shared__ int redo_flag;
