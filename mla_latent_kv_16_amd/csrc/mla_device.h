@@ -33,7 +33,7 @@ constexpr int kKvBlock = 32;                       // kv rows per MFMA block (S^
 constexpr int kQStepsPerWave = kRow / 16 / 2;      // 18 MFMA k-steps: half the 576-wide row
 constexpr int kColTilesPerWave = kNope / 32 / 2;   // 8 output column tiles of 32
 constexpr int kStageBytes = kKvBlock * kRowBytes;  // 36,864: half a page
-constexpr int kStages = 3;                         // LDS ring depth
+constexpr int kStages = 4;                         // LDS ring depth (two blocks in flight)
 constexpr int kStageCopiesPerWave = 9;             // 16-byte-per-lane copies per wave per block
 constexpr int kCombineThreads = 256;
 
@@ -89,7 +89,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // completion is awaited explicitly with wait_vmem_all() before the barrier that
 // publishes a slot.  M0 is reserved to the compiler, which on gfx9 and later sets
 // it only for instructions these kernels do not use (LDS-DMA builtins, message
-// sends, indirect register indexing), so the asm may overwrite it.  Both are passed through readfirstlane (as unsigned 32-bit
+// sends, indirect register indexing), so the asm may overwrite it.  A write of M0
+// needs one wait state before a global load with the LDS bit reads it.  Both are passed through readfirstlane (as unsigned 32-bit
 // halves) so that they are scalar operands even where the compiler cannot prove
 // them uniform.
 __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
@@ -98,7 +99,7 @@ __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint3
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
   const void* sbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds)
                : "memory");

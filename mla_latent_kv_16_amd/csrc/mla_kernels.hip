@@ -39,7 +39,6 @@ namespace mla {
 // exceed it.  The final normalisation uses the same m_ref as the sums, so the
 // result does not depend on which reference was used.
 constexpr float kLazyRescale = 32.0f;
-constexpr int kBtCache = 256;  // block-table entries cached in LDS per refill
 constexpr float kLn2 = 0.69314718055994531f;
 
 struct WaveState {
@@ -180,14 +179,15 @@ __device__ __forceinline__ void store_partial(f32x4* xs, const f32x16& s) {
 }
 
 // One iteration.  `own` and `partner` are the two halves of block i's S^T in LDS
-// (this wave's and the other wave's of the pair); xs_next receives this wave's half
-// of block i + 1 (when HAS_NEXT).  `lim` is the number of leading rows of block i
-// this lane's query row may see.
+// (this wave's and the other wave's of the pair).  When HAS_NEXT, this wave's half
+// of block i + 1 replaces its half of block i in `own`, after a workgroup barrier
+// that follows every wave's reads of block i's halves.  `lim` is the number of
+// leading rows of block i this lane's query row may see.
 template <bool HAS_NEXT>
 __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk_next,
                                           const ReadBases& rb, const bf16x8* qreg,
-                                          const f32x4* own, const f32x4* partner, f32x4* xs_next,
-                                          WaveState& ws, int lim, float scale_log2) {
+                                          f32x4* own, const f32x4* partner, WaveState& ws,
+                                          int lim, float scale_log2) {
   const int lane = threadIdx.x & 63;
   constexpr int DQ = 4;                      // A-operand reads in flight
   constexpr int DV = 4;                      // V-operand read pairs in flight
@@ -284,6 +284,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
         vb1[u] = pv_read(u, 1);
       }
     }
+    if (HAS_NEXT && kk == kQStepsPerWave - 1) __syncthreads();  // block i's halves are read
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -299,7 +300,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
       vb1[u] = pv_read(t + DV, 1);
     }
     if constexpr (HAS_NEXT) {
-      if (t == 8) store_partial(xs_next, n0);  // block i + 1's half is complete
+      if (t == 8) store_partial(own, n0);  // block i + 1's half is complete
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -337,21 +338,27 @@ __device__ __forceinline__ void write_rows(const SplitArgs& a, const WaveState& 
   }
 }
 
-// Fill the LDS block-table cache with the physical pages of logical pages
-// [first, min(first + kBtCache, end)) of request b; out-of-range ids are clamped
-// to page 0 and flagged.  Ends in a barrier.
-__device__ __forceinline__ void fill_bt_cache(const SplitArgs& a, int* bt_cache, int b, int first,
+// Physical pages of 64 consecutive logical pages of one request, one per lane: a
+// wave looks up page pg with a lane read and refills the window on its own (no LDS,
+// no barrier).  Out-of-range ids are clamped to page 0 and flagged.
+struct PageIds {
+  int id;     // lane l: physical page of logical page first + l
+  int first;  // wave-uniform
+};
+
+__device__ __forceinline__ void load_page_ids(const SplitArgs& a, PageIds& pi, int b, int first,
                                               int end) {
-  const int idx = first + (int)threadIdx.x;
-  if (threadIdx.x < kBtCache && idx < end) {
-    int phys = a.block_table[(size_t)b * a.max_pages + idx];
+  const int idx = first + (int)(threadIdx.x & 63);
+  int phys = 0;
+  if (idx < end) {
+    phys = a.block_table[(size_t)b * a.max_pages + idx];
     if (phys < 0 || (int64_t)phys >= a.num_pages) {
       atomicOr(a.flags, kFlagBadPageId);
       phys = 0;
     }
-    bt_cache[threadIdx.x] = phys;
   }
-  __syncthreads();
+  pi.id = phys;
+  pi.first = first;
 }
 
 // Ring slot of block i.  The byte offset is passed through an empty asm so that the
@@ -363,33 +370,36 @@ __device__ __forceinline__ uint8_t* ring_slot(uint8_t* ring, int i) {
   return ring + off;
 }
 
-// Loads this wave's share of block i of the piece (logical pages [lo, hi) of request
-// b, visible length L) into registers, refilling the block-table cache when the
-// block's page is not in it (workgroup-uniform, ends in a barrier).
 // Starts the copy of block i of the piece (logical page lo + i / 2, half i % 2) into
-// ring slot i % kStages.  Refilling the block-table cache is workgroup-uniform and
-// ends in a barrier.
+// ring slot i % kStages.
 __device__ __forceinline__ void issue_block(const SplitArgs& a, uint8_t* ring,
-                                            const StageOffsets& so, int* bt_cache,
-                                            int& bt_first, int b, int lo, int hi, int L, int i) {
+                                            const StageOffsets& so, PageIds& pi, int b, int lo,
+                                            int hi, int L, int i) {
   const int pg = lo + (i >> 1), half = i & 1;
-  if (pg - bt_first >= kBtCache || pg < bt_first) {
-    bt_first = pg;
-    fill_bt_cache(a, bt_cache, b, bt_first, hi);
-  }
-  const uint32_t phys = __builtin_amdgcn_readfirstlane(bt_cache[pg - bt_first]);
+  if (pg - pi.first >= 64 || pg < pi.first) load_page_ids(a, pi, b, pg, hi);
+  const uint32_t phys = __builtin_amdgcn_readlane(pi.id, pg - pi.first);
   const int valid = min(kKvBlock, L - pg * kPage - half * kKvBlock);
   const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_pool) +
                        ((size_t)phys * kPageBytes + (size_t)half * kStageBytes);
   stage_block(src, ring_slot(ring, i), valid, so);
 }
 
+// Waits until at most n of this wave's block copies are in flight (n = 0 or 1
+// blocks of kStageCopiesPerWave copies; copies complete in issue order).
+__device__ __forceinline__ void wait_blocks_in_flight(int n) {
+  static_assert(kStageCopiesPerWave == 9, "vmcnt immediates below");
+  if (n > 0)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    wait_vmem_all();
+}
+
 // One piece: logical pages [lo, hi) of request b against M-tile mt.  The pages are
-// walked as 32-row blocks through a ring of kStages half-page stages, two blocks
-// ahead of the one being scored.
-__device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32x4* xbuf,
-                                          int* bt_cache, int* redo_flag, int b, int mt, int lo,
-                                          int hi, bool whole, int slot) {
+// walked as 32-row blocks through a ring of kStages half-page slots: while block i
+// is scored (softmax, P V) and block i + 1's S^T is computed, blocks i + 2 and i + 3
+// are in flight.
+__device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32x4* xbuf, int b,
+                                          int mt, int lo, int hi, bool whole, int slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = wave >> 1, c = wave & 1;  // row slice of the M-tile; contraction / column half
   const int M = a.M;
@@ -426,11 +436,13 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   ws.m_seen = -INFINITY;
   const ReadBases rb = read_bases(c);
   const StageOffsets so = stage_offsets();
-  int bt_first = lo;
-  fill_bt_cache(a, bt_cache, b, bt_first, hi);
+  PageIds pi;
+  load_page_ids(a, pi, b, lo, hi);
+  wait_vmem_all();  // queries and page ids are in before any block copy is counted
 
-  // xbuf holds two parities x four waves of S^T halves (4 x 64 lanes x f32x4 each)
-  auto xslot = [&](int parity, int w) { return xbuf + (parity * kWaves + w) * 4 * 64; };
+  f32x4* own = xbuf + wave * 4 * 64;  // this wave's S^T half (4 x 64 lanes x f32x4)
+  const f32x4* partner = xbuf + (wave ^ 1) * 4 * 64;
+  auto lim_of = [&](int i) { return n_vis - (lo + (i >> 1)) * kPage - (i & 1) * kKvBlock; };
 
   // At most two passes: the second (rare) one starts from the rows' true maxima.
   for (int pass = 0; pass < 2; ++pass) {
@@ -439,44 +451,47 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     ws.m_ref = pass == 0 ? -INFINITY : ws.m_seen;
     ws.l_run = 0.0f;
     ws.l_bf = 0.0f;
-    // Block j is copied into ring slot j % 3 from the start of iteration j - 2 (the
-    // slot's previous block, j - 3, was finished in iteration j - 3), its S^T halves
+    // Block j is copied into ring slot j % 4 from the start of iteration j - 3 (the
+    // slot's previous block, j - 4, was finished in iteration j - 4), its S^T halves
     // are computed in iteration j - 1 and its softmax and P V run in iteration j.
-    // Prologue: blocks 0 and 1 in flight, S^T halves of block 0.
-    if (nb > 0) issue_block(a, ring, so, bt_cache, bt_first, b, lo, hi, L, 0);
-    if (nb > 1) issue_block(a, ring, so, bt_cache, bt_first, b, lo, hi, L, 1);
-    wait_vmem_all();
-    __syncthreads();  // blocks 0 and 1 are in LDS
-    if (nb > 0) store_partial(xslot(0, wave), qk_partial(ring_slot(ring, 0), rb, qreg));
-    // iteration i: wait for block i + 1, publish it and both S^T halves of block i,
-    // and start block i + 2 into the slot block i - 1 has left
-    auto top = [&](int i) {
+    // Prologue: blocks 0..2 in flight, S^T halves of block 0.
+#pragma unroll 1
+    for (int j = 0; j < 3 && j < nb; ++j) issue_block(a, ring, so, pi, b, lo, hi, L, j);
+    if (nb >= 3)
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (nb == 2)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
       wait_vmem_all();
-      __syncthreads();
-      if (i + 2 < nb) issue_block(a, ring, so, bt_cache, bt_first, b, lo, hi, L, i + 2);
-    };
-    auto lim_of = [&](int i) { return n_vis - (lo + (i >> 1)) * kPage - (i & 1) * kKvBlock; };
+    __syncthreads();  // block 0 is in LDS
+    if (nb > 0) store_partial(own, qk_partial(ring_slot(ring, 0), rb, qreg));
     int i = 0;
     for (; i + 1 < nb; ++i) {
-      top(i);
-      pipe_step<true>(ring_slot(ring, i), ring_slot(ring, i + 1), rb, qreg, xslot(i & 1, wave),
-                      xslot(i & 1, wave ^ 1), xslot((i + 1) & 1, wave), ws, lim_of(i),
-                      a.scale_log2);
+      // block i + 1 has landed (block i + 2 may still be in flight) ...
+      wait_blocks_in_flight(i + 2 < nb ? 1 : 0);
+      // ... in every wave; both S^T halves of block i are in LDS; every wave is done
+      // with block i - 1, whose slot now receives block i + 3
+      __syncthreads();
+      if (i + 3 < nb) issue_block(a, ring, so, pi, b, lo, hi, L, i + 3);
+      pipe_step<true>(ring_slot(ring, i), ring_slot(ring, i + 1), rb, qreg, own, partner, ws,
+                      lim_of(i), a.scale_log2);
     }
-    if (i < nb) {
-      top(i);
-      pipe_step<false>(ring_slot(ring, i), nullptr, rb, qreg, xslot(i & 1, wave),
-                       xslot(i & 1, wave ^ 1), nullptr, ws, lim_of(i), a.scale_log2);
+    if (i < nb) {  // the last block: nothing left to score ahead or to copy
+      __syncthreads();
+      pipe_step<false>(ring_slot(ring, i), nullptr, rb, qreg, own, partner, ws, lim_of(i),
+                       a.scale_log2);
     }
     // a row whose scores outgrew its reference by more than the lazy bound forces a
-    // second pass for the whole workgroup
+    // second pass for the whole workgroup; the flag lives in the exchange buffer
     const bool broke = ws.m_ref != -INFINITY && ws.m_seen > ws.m_ref + kLazyRescale;
+    int* redo_flag = reinterpret_cast<int*>(xbuf);
+    __syncthreads();  // every wave is done with the ring and the exchange buffer
     if (threadIdx.x == 0) *redo_flag = 0;
-    __syncthreads();  // every wave is done with the ring and the exchange slots
+    __syncthreads();
     if (__builtin_amdgcn_ballot_w64(broke) && lane == 0) *redo_flag = 1;
     __syncthreads();
     const bool redo = *redo_flag != 0;
-    __syncthreads();  // the flag has been read before anyone resets it
+    __syncthreads();  // the flag has been read before the buffer is reused
     if (!redo) break;
   }
 
@@ -486,38 +501,47 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 splitkv_kernel(SplitArgs a) {
+  // 4 x 36 KB ring + 16 KB exchange buffer = the whole 160 KB of LDS
   __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
-  __shared__ f32x4 xbuf[2 * kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
-  __shared__ int prefix[kMaxBatch + 1];
-  __shared__ int bt_cache[kBtCache];
-  __shared__ int redo_flag;
+  __shared__ f32x4 xbuf[kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
+  static_assert(sizeof(f32x4) * kWaves * 4 * 64 >= (kMaxBatch + 1) * sizeof(int),
+                "the page prefix is built in the exchange buffer");
 
   const int lam = xcd_logical_id(blockIdx.x, gridDim.x);
   const int g = lam / a.n_mt;
   const int mt = lam - g * a.n_mt;
 
+  // page prefix of the batch, in the exchange buffer until the first piece starts
+  int* prefix = reinterpret_cast<int*>(xbuf);
   build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, true);
   const int64_t T = prefix[a.B];
   const int64_t p0 = part_begin(T, a.G, g);
   const int64_t p1 = part_begin(T, a.G, g + 1);
-  if (p0 >= p1) return;
-
   // first request whose pages reach past p0
   int lo = 0, hi = a.B - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (prefix[mid + 1] > p0) hi = mid; else lo = mid + 1;
   }
-  for (int b = lo; b < a.B && prefix[b] < p1; ++b) {
-    const int pb0 = prefix[b], pb1 = prefix[b + 1];
-    if (pb1 <= pb0) continue;
-    const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
-    const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
-    const bool whole = plo == 0 && phi == pb1 - pb0;
-    run_piece(a, ring, xbuf, bt_cache, &redo_flag, __builtin_amdgcn_readfirstlane(b), mt,
-              __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi), whole,
-              (b + g) * a.n_mt + mt);
-    __syncthreads();  // LDS free before the next piece stages into it
+  int pb0 = prefix[lo];
+  __syncthreads();  // the prefix has been read
+  if (p0 >= p1) return;
+
+  // walk the requests the partition touches; a request's page count is recomputed
+  // from its clamped length (the same count the prefix was built from)
+  for (int b = lo; b < a.B && pb0 < p1; ++b) {
+    const int Lb = clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
+    const int pb1 = pb0 + (Lb + kPage - 1) / kPage;
+    if (pb1 > pb0) {
+      const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
+      const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
+      const bool whole = plo == 0 && phi == pb1 - pb0;
+      run_piece(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b), mt,
+                __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi), whole,
+                (b + g) * a.n_mt + mt);
+      __syncthreads();  // LDS free before the next piece stages into it
+    }
+    pb0 = pb1;
   }
 }
 
