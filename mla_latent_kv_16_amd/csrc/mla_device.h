@@ -144,10 +144,12 @@ __device__ __forceinline__ int clamp_len(int L, int Sq, int max_pages, uint32_t*
   return L;
 }
 
-// Fills prefix[0..B] (LDS) with the page prefix sums of the clamped lengths.
-// Wave 0 scans; every thread of the workgroup must call it (it ends in a barrier).
+// Fills prefix[0..B] (LDS) with the page prefix sums of the clamped lengths, and
+// lens[0..B) with those lengths when lens is given.  Wave 0 scans; every thread of
+// the workgroup must call it (it ends in a barrier).
 __device__ inline void build_page_prefix(const int32_t* seq_lens, int B, int Sq, int max_pages,
-                                         int* prefix, uint32_t* flags, bool report) {
+                                         int* prefix, uint32_t* flags, bool report,
+                                         int* lens = nullptr) {
   const int tid = threadIdx.x;
   if (tid < 64) {  // wave 0
     const int per = (B + 63) / 64;
@@ -168,6 +170,7 @@ __device__ inline void build_page_prefix(const int32_t* seq_lens, int B, int Sq,
     for (int b = b0; b < b1; ++b) {
       prefix[b] = run;
       const int L = clamp_len(seq_lens[b], Sq, max_pages, flags, false);
+      if (lens) lens[b] = L;
       run += (L + kPage - 1) / kPage;
     }
     if (tid == 63) prefix[B] = incl;

@@ -142,6 +142,23 @@ __device__ __forceinline__ ReadBases read_bases(int c) {
   return rb;
 }
 
+// ---- block copies issued from inside the pipeline step -------------------------
+// The vector memory path takes a wave's nine copies of a block only at its own pace
+// (hundreds of cycles), so the step issues them one per two S^T MFMAs instead of in
+// a burst at the top of the iteration.  A step always issues nine copies: when no
+// whole block is due, the job re-copies the block being scored into its own slot
+// (a whole block: only a request's last block can be partial, and it is never
+// scored ahead of another block), which writes the bytes already there.
+struct CopyJob {
+  const uint8_t* src;  // first row of the block in the pool (wave-uniform)
+  uint32_t dst;        // LDS address of this wave's 8 rows in the block's slot
+};
+
+__device__ __forceinline__ CopyJob copy_job(const uint8_t* src, uint8_t* slot) {
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return CopyJob{src, lds_addr(slot) + 8 * wave * kRowBytes};
+}
+
 // ---- the software pipeline --------------------------------------------------------
 // Iteration i of a piece runs the softmax step and O += P V of block i while the MFMA
 // pipe computes this wave's half of S^T = K Q^T for block i + 1.  A wave pair owns 32
@@ -187,7 +204,8 @@ template <bool HAS_NEXT>
 __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk_next,
                                           const ReadBases& rb, const bf16x8* qreg,
                                           f32x4* own, const f32x4* partner, WaveState& ws,
-                                          int lim, float scale_log2) {
+                                          int lim, float scale_log2, const CopyJob& job,
+                                          const StageOffsets& so) {
   const int lane = threadIdx.x & 63;
   constexpr int DQ = 4;                      // A-operand reads in flight
   constexpr int DV = 4;                      // V-operand read pairs in flight
@@ -224,6 +242,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
     if constexpr (HAS_NEXT) {
       n0 = mfma32(abuf[kk % DQ], qreg[kk], n0);
       if (kk + DQ < kQStepsPerWave) abuf[kk % DQ] = qk_read(kk + DQ);
+      if (kk & 1) dma16(job.src, so.off[kk >> 1], job.dst + (kk >> 1) * 1024);
     }
     if (kk == 0) {
       // full scores: own half + partner half (the same sum on both waves of the pair,
@@ -370,28 +389,24 @@ __device__ __forceinline__ uint8_t* ring_slot(uint8_t* ring, int i) {
   return ring + off;
 }
 
-// Starts the copy of block i of the piece (logical page lo + i / 2, half i % 2) into
-// ring slot i % kStages.
-__device__ __forceinline__ void issue_block(const SplitArgs& a, uint8_t* ring,
-                                            const StageOffsets& so, PageIds& pi, int b, int lo,
-                                            int hi, int L, int i) {
+// Pool address of block i of the piece (logical page lo + i / 2, half i % 2) and the
+// number of its rows inside the request.
+__device__ __forceinline__ const uint8_t* block_source(const SplitArgs& a, PageIds& pi, int b,
+                                                       int lo, int hi, int L, int i,
+                                                       int& valid) {
   const int pg = lo + (i >> 1), half = i & 1;
   if (pg - pi.first >= 64 || pg < pi.first) load_page_ids(a, pi, b, pg, hi);
   const uint32_t phys = __builtin_amdgcn_readlane(pi.id, pg - pi.first);
-  const int valid = min(kKvBlock, L - pg * kPage - half * kKvBlock);
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_pool) +
-                       ((size_t)phys * kPageBytes + (size_t)half * kStageBytes);
-  stage_block(src, ring_slot(ring, i), valid, so);
+  valid = min(kKvBlock, L - pg * kPage - half * kKvBlock);
+  return reinterpret_cast<const uint8_t*>(a.kv_pool) +
+         ((size_t)phys * kPageBytes + (size_t)half * kStageBytes);
 }
 
-// Waits until at most n of this wave's block copies are in flight (n = 0 or 1
-// blocks of kStageCopiesPerWave copies; copies complete in issue order).
-__device__ __forceinline__ void wait_blocks_in_flight(int n) {
-  static_assert(kStageCopiesPerWave == 9, "vmcnt immediates below");
-  if (n > 0)
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else
-    wait_vmem_all();
+// Waits until at most one step's worth of this wave's copies (kStageCopiesPerWave)
+// is in flight; copies complete in issue order.
+__device__ __forceinline__ void wait_all_but_one_block() {
+  static_assert(kStageCopiesPerWave == 9, "vmcnt immediate below");
+  asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
 }
 
 // One piece: logical pages [lo, hi) of request b against M-tile mt.  The pages are
@@ -399,14 +414,13 @@ __device__ __forceinline__ void wait_blocks_in_flight(int n) {
 // is scored (softmax, P V) and block i + 1's S^T is computed, blocks i + 2 and i + 3
 // are in flight.
 __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32x4* xbuf, int b,
-                                          int mt, int lo, int hi, bool whole, int slot) {
+                                          int L, int mt, int lo, int hi, bool whole, int slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = wave >> 1, c = wave & 1;  // row slice of the M-tile; contraction / column half
   const int M = a.M;
   const int m_slice = mt * kMTile + p * kRowsPerWave;
   const int m_q = m_slice + (lane & 31);  // the query row this lane scores
   const bool q_ok = m_q < M;
-  const int L = clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
   const int t = q_ok ? m_q / a.H : 0;
   const int n_vis = a.causal ? L - a.Sq + t + 1 : L;
   // rows the M-tile's last query row sees: blocks past it are skipped by every wave
@@ -451,12 +465,24 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     ws.m_ref = pass == 0 ? -INFINITY : ws.m_seen;
     ws.l_run = 0.0f;
     ws.l_bf = 0.0f;
-    // Block j is copied into ring slot j % 4 from the start of iteration j - 3 (the
-    // slot's previous block, j - 4, was finished in iteration j - 4), its S^T halves
-    // are computed in iteration j - 1 and its softmax and P V run in iteration j.
+    // Block j is copied into ring slot j % 4 during iteration j - 3 (the slot's
+    // previous block, j - 4, was finished in iteration j - 4), its S^T halves are
+    // computed in iteration j - 1 and its softmax and P V run in iteration j.  A
+    // request's partial last block is copied at the top of iteration j - 3 instead.
     // Prologue: blocks 0..2 in flight, S^T halves of block 0.
+    wait_vmem_all();  // no copy of an earlier pass is still landing in the ring
+    const uint8_t* src_cur = nullptr;  // pool address of block i
+    const uint8_t* src_next = nullptr;  // ... of block i + 1
+    const uint8_t* src_ahead = nullptr;  // ... of block i + 2
 #pragma unroll 1
-    for (int j = 0; j < 3 && j < nb; ++j) issue_block(a, ring, so, pi, b, lo, hi, L, j);
+    for (int j = 0; j < 3 && j < nb; ++j) {
+      int valid;
+      const uint8_t* src = block_source(a, pi, b, lo, hi, L, j, valid);
+      stage_block(src, ring_slot(ring, j), valid, so);
+      if (j == 0) src_cur = src;
+      if (j == 1) src_next = src;
+      if (j == 2) src_ahead = src;
+    }
     if (nb >= 3)
       asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
     else if (nb == 2)
@@ -467,19 +493,35 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     if (nb > 0) store_partial(own, qk_partial(ring_slot(ring, 0), rb, qreg));
     int i = 0;
     for (; i + 1 < nb; ++i) {
-      // block i + 1 has landed (block i + 2 may still be in flight) ...
-      wait_blocks_in_flight(i + 2 < nb ? 1 : 0);
+      // block i + 1 has landed ...  (at least one step's copies were issued after
+      // it, except when the piece has only two blocks)
+      if (i == 0 && nb < 3)
+        wait_vmem_all();
+      else
+        wait_all_but_one_block();
       // ... in every wave; both S^T halves of block i are in LDS; every wave is done
       // with block i - 1, whose slot now receives block i + 3
       __syncthreads();
-      if (i + 3 < nb) issue_block(a, ring, so, pi, b, lo, hi, L, i + 3);
+      CopyJob job = copy_job(src_cur, ring_slot(ring, i));  // same-data re-copy
+      const uint8_t* src_new = nullptr;
+      if (i + 3 < nb) {
+        int valid;
+        src_new = block_source(a, pi, b, lo, hi, L, i + 3, valid);
+        if (valid == kKvBlock)
+          job = copy_job(src_new, ring_slot(ring, i + 3));
+        else
+          stage_block(src_new, ring_slot(ring, i + 3), valid, so);
+      }
       pipe_step<true>(ring_slot(ring, i), ring_slot(ring, i + 1), rb, qreg, own, partner, ws,
-                      lim_of(i), a.scale_log2);
+                      lim_of(i), a.scale_log2, job, so);
+      src_cur = src_next;
+      src_next = src_ahead;
+      src_ahead = src_new;
     }
-    if (i < nb) {  // the last block: nothing left to score ahead or to copy
+    if (i < nb) {  // the last block (already in LDS): nothing left to score ahead or copy
       __syncthreads();
       pipe_step<false>(ring_slot(ring, i), nullptr, rb, qreg, own, partner, ws, lim_of(i),
-                       a.scale_log2);
+                       a.scale_log2, CopyJob{}, so);
     }
     // a row whose scores outgrew its reference by more than the lazy bound forces a
     // second pass for the whole workgroup; the flag lives in the exchange buffer
@@ -504,16 +546,18 @@ splitkv_kernel(SplitArgs a) {
   // 4 x 36 KB ring + 16 KB exchange buffer = the whole 160 KB of LDS
   __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
   __shared__ f32x4 xbuf[kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
-  static_assert(sizeof(f32x4) * kWaves * 4 * 64 >= (kMaxBatch + 1) * sizeof(int),
-                "the page prefix is built in the exchange buffer");
+  static_assert(sizeof(f32x4) * kWaves * 4 * 64 >= (2 * kMaxBatch + 1) * sizeof(int),
+                "the page prefix and lengths are built in the exchange buffer");
 
   const int lam = xcd_logical_id(blockIdx.x, gridDim.x);
   const int g = lam / a.n_mt;
   const int mt = lam - g * a.n_mt;
 
-  // page prefix of the batch, in the exchange buffer until the first piece starts
+  // page prefix and clamped lengths of the batch, in the exchange buffer until the
+  // first piece starts
   int* prefix = reinterpret_cast<int*>(xbuf);
-  build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, true);
+  int* lens = prefix + kMaxBatch + 1;
+  build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, true, lens);
   const int64_t T = prefix[a.B];
   const int64_t p0 = part_begin(T, a.G, g);
   const int64_t p1 = part_begin(T, a.G, g + 1);
@@ -524,19 +568,21 @@ splitkv_kernel(SplitArgs a) {
     if (prefix[mid + 1] > p0) hi = mid; else lo = mid + 1;
   }
   int pb0 = prefix[lo];
+  const int L_first = lens[lo];
   __syncthreads();  // the prefix has been read
   if (p0 >= p1) return;
 
   // walk the requests the partition touches; a request's page count is recomputed
   // from its clamped length (the same count the prefix was built from)
   for (int b = lo; b < a.B && pb0 < p1; ++b) {
-    const int Lb = clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
+    const int Lb = b == lo ? L_first : clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
     const int pb1 = pb0 + (Lb + kPage - 1) / kPage;
     if (pb1 > pb0) {
       const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
       const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
       const bool whole = plo == 0 && phi == pb1 - pb0;
-      run_piece(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b), mt,
+      run_piece(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
+                __builtin_amdgcn_readfirstlane(Lb), mt,
                 __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi), whole,
                 (b + g) * a.n_mt + mt);
       __syncthreads();  // LDS free before the next piece stages into it
@@ -572,13 +618,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
-// One workgroup per folded query row (b, m) of a split request.  Thread t handles
-// columns 8 (t % 64) .. + 8 of every fourth piece starting at t / 64; the four
-// piece lanes are summed through LDS.
+// Combine, many pieces per request (G >= 16 B): one workgroup per folded query row
+// (b, m) of a split request.  Thread t handles columns 8 (t % 64) .. + 8 of the
+// pieces s with s % 4 == t / 64.  The partial outputs of a chunk of 64 pieces (16
+// per thread) are all requested at once, before the row's log-sum-exp over the
+// pieces is reduced, so that one memory round trip covers both; the four piece
+// lanes are summed through LDS.
+constexpr int kCombineLanes = kCombineThreads / 64;
+constexpr int kCombineChunk = 16;  // pieces per thread per chunk
+
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
   __shared__ int prefix[kMaxBatch + 1];
-  __shared__ float red[kCombineThreads / 64];
-  __shared__ __attribute__((aligned(16))) float part[kCombineThreads / 64][64 * 8];
+  __shared__ float red[kCombineLanes];
+  __shared__ __attribute__((aligned(16))) float part[kCombineLanes][64 * 8];
   build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, false);
   const int64_t T = prefix[a.B];
   const int row = blockIdx.x;
@@ -591,14 +643,41 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
   const int mt = m / a.MT, ml = m - mt * a.MT;
   const int n = g1 - g0 + 1;
   // Partitions g0..g1 hold the request's pieces.  With more partitions than pages
-  // some partitions are empty; they wrote nothing and carry no weight.
+  // some partitions are empty; they wrote nothing and carry no weight.  With at
+  // least one page per partition (G <= T) none is empty and the 64-bit divisions
+  // that find empty ones are skipped.
+  const bool dense = (int64_t)a.G <= T;
   auto lse_of = [&](int s) {
     const int g = g0 + s;
-    if (part_begin(T, a.G, g) >= part_begin(T, a.G, g + 1)) return -INFINITY;
+    if (!dense && part_begin(T, a.G, g) >= part_begin(T, a.G, g + 1)) return -INFINITY;
     const size_t slot = (size_t)(b + g) * a.n_mt + mt;
     return a.part_lse[slot * a.slot_rows + ml];
   };
   const int tid = threadIdx.x;
+  const int cg = tid & 63, pl = tid >> 6;
+  auto src_of = [&](int s) {
+    const size_t slot = (size_t)(b + g0 + s) * a.n_mt + mt;
+    return a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * cg;
+  };
+
+  f32x4 v0[kCombineChunk], v1[kCombineChunk];
+  float lv[kCombineChunk];
+  auto load_chunk = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kCombineChunk; ++u) {
+      const int s = s0 + pl + kCombineLanes * u;
+      lv[u] = -INFINITY;
+      if (s < n) {
+        const float* src = src_of(s);
+        v0[u] = *reinterpret_cast<const f32x4*>(src);
+        v1[u] = *reinterpret_cast<const f32x4*>(src + 4);
+        lv[u] = lse_of(s);
+      }
+    }
+  };
+  load_chunk(0);
+
+  // the row's log2-sum-exp2 over its pieces
   float mx = -INFINITY;
   for (int s = tid; s < n; s += kCombineThreads) mx = fmaxf(mx, lse_of(s));
   mx = block_max(mx, red);
@@ -609,23 +688,116 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
   const bool seen = tot > 0.0f;
   const float lse2 = seen ? mx + log2f(tot) : -INFINITY;
 
-  const int cg = tid & 63, pl = tid >> 6;
-  constexpr int kLanes = kCombineThreads / 64;
+  f32x4 o0 = {}, o1 = {};
+  auto accumulate = [&]() {
+#pragma unroll
+    for (int u = 0; u < kCombineChunk; ++u) {
+      const float w = (seen && lv[u] != -INFINITY) ? exp2f(lv[u] - lse2) : 0.0f;
+      // a zero-weight slot may hold stale data, even NaN: select, never multiply
+      o0 = w != 0.0f ? o0 + w * v0[u] : o0;
+      o1 = w != 0.0f ? o1 + w * v1[u] : o1;
+    }
+  };
+  accumulate();
+  for (int s0 = kCombineLanes * kCombineChunk; s0 < n; s0 += kCombineLanes * kCombineChunk) {
+    load_chunk(s0);
+    accumulate();
+  }
+
+  *reinterpret_cast<f32x4*>(&part[pl][8 * cg]) = o0;
+  *reinterpret_cast<f32x4*>(&part[pl][8 * cg + 4]) = o1;
+  __syncthreads();
+  if (pl == 0) {
+#pragma unroll
+    for (int q = 1; q < kCombineLanes; ++q) {
+      o0 += *reinterpret_cast<const f32x4*>(&part[q][8 * cg]);
+      o1 += *reinterpret_cast<const f32x4*>(&part[q][8 * cg + 4]);
+    }
+    float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * cg;
+    *reinterpret_cast<f32x4*>(dst) = o0;
+    *reinterpret_cast<f32x4*>(dst + 4) = o1;
+    if (cg == 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
+  }
+}
+
+// Combine, few pieces per request: one wave per folded query row, four rows per
+// workgroup, no LDS and no barriers.  The wave finds its request's page range by
+// summing the clamped page counts itself, reduces the row's log-sum-exp over the
+// pieces with lane shuffles, and lane l accumulates columns 8 l .. 8 l + 7 over all
+// pieces, four pieces' loads in flight at a time.
+constexpr int kRowsPerCombineGroup = kCombineThreads / 64;
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sumf(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__global__ void __launch_bounds__(kCombineThreads) combine_rows_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerCombineGroup + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.B * a.M) return;  // the whole wave
+  const int b = (int)(row / a.M), m = (int)(row - (int64_t)b * a.M);
+  int below = 0, total = 0;
+  for (int j = lane; j < a.B; j += 64) {
+    const int L = clamp_len(a.seq_lens[j], a.Sq, a.max_pages, a.flags, false);
+    const int pages = (L + kPage - 1) / kPage;
+    total += pages;
+    if (j < b) below += pages;
+  }
+  const int64_t T = wave_sum(total);
+  const int Lb = clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
+  const int pb0 = wave_sum(below), pb1 = pb0 + (Lb + kPage - 1) / kPage;
+  if (pb1 <= pb0) return;
+  const int g0 = part_of(T, a.G, pb0);
+  const int g1 = part_of(T, a.G, pb1 - 1);
+  if (g0 == g1) return;  // one partition held the whole request: already final
+  const int mt = m / a.MT, ml = m - mt * a.MT;
+  const int n = g1 - g0 + 1;
+  const bool dense = (int64_t)a.G <= T;  // then no partition is empty
+  auto lse_of = [&](int s) {
+    const int g = g0 + s;
+    if (!dense && part_begin(T, a.G, g) >= part_begin(T, a.G, g + 1)) return -INFINITY;
+    const size_t slot = (size_t)(b + g) * a.n_mt + mt;
+    return a.part_lse[slot * a.slot_rows + ml];
+  };
+  float mx = -INFINITY;
+  for (int s = lane; s < n; s += 64) mx = fmaxf(mx, lse_of(s));
+  mx = wave_max(mx);
+  float tot = 0.0f;
+  if (mx != -INFINITY)
+    for (int s = lane; s < n; s += 64) tot += exp2f(lse_of(s) - mx);
+  tot = wave_sumf(tot);
+  const bool seen = tot > 0.0f;
+  const float lse2 = seen ? mx + log2f(tot) : -INFINITY;
+
   f32x4 o0 = {}, o1 = {};
   constexpr int U = 4;
-  int s = pl;
-  for (; s + kLanes * (U - 1) < n; s += kLanes * U) {
+  for (int s0 = 0; s0 < n; s0 += U) {
     f32x4 v0[U], v1[U];
     float w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int su = s + kLanes * u;
-      const size_t slot = (size_t)(b + g0 + su) * a.n_mt + mt;
-      const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * cg;
-      v0[u] = *reinterpret_cast<const f32x4*>(src);
-      v1[u] = *reinterpret_cast<const f32x4*>(src + 4);
-      const float l = lse_of(su);
-      w[u] = (seen && l != -INFINITY) ? exp2f(l - lse2) : 0.0f;
+      const int s = s0 + u;
+      w[u] = 0.0f;
+      if (s < n) {
+        const size_t slot = (size_t)(b + g0 + s) * a.n_mt + mt;
+        const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * lane;
+        v0[u] = *reinterpret_cast<const f32x4*>(src);
+        v1[u] = *reinterpret_cast<const f32x4*>(src + 4);
+        const float l = lse_of(s);
+        w[u] = (seen && l != -INFINITY) ? exp2f(l - lse2) : 0.0f;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -634,30 +806,10 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
       o1 = w[u] != 0.0f ? o1 + w[u] * v1[u] : o1;
     }
   }
-  for (; s < n; s += kLanes) {
-    const float l = lse_of(s);
-    const float w = (seen && l != -INFINITY) ? exp2f(l - lse2) : 0.0f;
-    if (w != 0.0f) {
-      const size_t slot = (size_t)(b + g0 + s) * a.n_mt + mt;
-      const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * cg;
-      o0 += w * *reinterpret_cast<const f32x4*>(src);
-      o1 += w * *reinterpret_cast<const f32x4*>(src + 4);
-    }
-  }
-  *reinterpret_cast<f32x4*>(&part[pl][8 * cg]) = o0;
-  *reinterpret_cast<f32x4*>(&part[pl][8 * cg + 4]) = o1;
-  __syncthreads();
-  if (pl == 0) {
-#pragma unroll
-    for (int p = 1; p < kLanes; ++p) {
-      o0 += *reinterpret_cast<const f32x4*>(&part[p][8 * cg]);
-      o1 += *reinterpret_cast<const f32x4*>(&part[p][8 * cg + 4]);
-    }
-    float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * cg;
-    *reinterpret_cast<f32x4*>(dst) = o0;
-    *reinterpret_cast<f32x4*>(dst + 4) = o1;
-    if (cg == 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
-  }
+  float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * lane;
+  *reinterpret_cast<f32x4*>(dst) = o0;
+  *reinterpret_cast<f32x4*>(dst + 4) = o1;
+  if (lane == 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
 }
 
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream) {
@@ -670,7 +822,14 @@ hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.M;
   if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, a);
+  // about G / B pieces per request: spread many over a workgroup, few over a wave
+  if ((int64_t)a.G >= 16 * (int64_t)a.B) {
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, a);
+  } else {
+    const int64_t groups = (rows + kRowsPerCombineGroup - 1) / kRowsPerCombineGroup;
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)groups), dim3(kCombineThreads), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 

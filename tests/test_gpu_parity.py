@@ -134,6 +134,33 @@ def test_more_partitions_than_pages():
     check(O, lse, *oracle(w), "parts>pages")
 
 
+def _shorten(w, lens):
+    """Cuts requests 1.. of a fixed-length workload short (their pages stay valid)."""
+    w.seq_lens = w.seq_lens.copy()
+    w.seq_lens[1:] = lens
+    return w
+
+
+COMBINE_CASES = [
+    # (name, workload kwargs, later lengths or None, partitions): both combine kernels,
+    # each with more than one chunk / lane sweep of pieces and with empty partitions
+    ("pieces-per-group-long", dict(seed=121, B=1, Sq=4, H=16, lens=("fixed", 64 * 130)), None, 100),
+    ("pieces-per-group-empty", dict(seed=122, B=1, Sq=4, H=16, lens=("fixed", 200)), None, 20),
+    ("pieces-per-wave-long", dict(seed=123, B=5, Sq=4, H=16, lens=("fixed", 64 * 120)),
+     [70, 200, 64, 5], 79),
+    ("pieces-per-wave-empty", dict(seed=124, B=3, Sq=2, H=16, lens=("fixed", 150)), None, 40),
+]
+
+
+@pytest.mark.parametrize("name,kw,later,parts", COMBINE_CASES, ids=[c[0] for c in COMBINE_CASES])
+def test_combine_paths(name, kw, later, parts):
+    w = make_workload("tiny", **kw)
+    if later is not None:
+        w = _shorten(w, later)
+    O, lse = run(w, parts=parts)
+    check(O, lse, *oracle(w), name)
+
+
 def test_split_and_combine_entry_points_equal_decode():
     w = make_workload("tiny", seed=113, B=2, Sq=4, H=16, lens=("uniform", 600, 1200))
     dev = to_dev(w)
