@@ -195,17 +195,17 @@ __device__ __forceinline__ void store_partial(f32x4* xs, const f32x16& s) {
     xs[j * 64 + lane] = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
 }
 
-// One iteration.  `own` and `partner` are the two halves of block i's S^T in LDS
-// (this wave's and the other wave's of the pair).  When HAS_NEXT, this wave's half
-// of block i + 1 replaces its half of block i in `own`, after a workgroup barrier
-// that follows every wave's reads of block i's halves.  `lim` is the number of
+// One iteration.  s_own is this wave's half of block i's S^T (kept in registers) and
+// `partner` the other wave's half in LDS.  When HAS_NEXT, this wave's half of block
+// i + 1 replaces s_own and its copy in `own` (read by the partner), after a
+// workgroup barrier that follows every wave's reads of block i's halves.  `lim` is the number of
 // leading rows of block i this lane's query row may see.
 template <bool HAS_NEXT>
 __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk_next,
                                           const ReadBases& rb, const bf16x8* qreg,
-                                          f32x4* own, const f32x4* partner, WaveState& ws,
-                                          int lim, float scale_log2, const CopyJob& job,
-                                          const StageOffsets& so) {
+                                          f32x16& s_own, f32x4* own, const f32x4* partner,
+                                          WaveState& ws, int lim, float scale_log2,
+                                          const CopyJob& job, const StageOffsets& so) {
   const int lane = threadIdx.x & 63;
   constexpr int DQ = 4;                      // A-operand reads in flight
   constexpr int DV = 4;                      // V-operand read pairs in flight
@@ -217,12 +217,9 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
     return lds_read_tr(blk + rb.v[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
   };
 
-  f32x4 ow[4], pr[4];
+  f32x4 pr[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ow[j] = own[j * 64 + lane];
-    pr[j] = partner[j * 64 + lane];
-  }
+  for (int j = 0; j < 4; ++j) pr[j] = partner[j * 64 + lane];
   bf16x8 abuf[DQ];
   if constexpr (HAS_NEXT) {
 #pragma unroll
@@ -250,7 +247,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * j + e] = ow[j][e] + pr[j][e];
+        for (int e = 0; e < 4; ++e) x[4 * j + e] = s_own[4 * j + e] + pr[j][e];
     } else if (kk == 2) {
       if (__builtin_amdgcn_ballot_w64(lim < kKvBlock)) {
 #pragma unroll
@@ -319,7 +316,10 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
       vb1[u] = pv_read(t + DV, 1);
     }
     if constexpr (HAS_NEXT) {
-      if (t == 8) store_partial(own, n0);  // block i + 1's half is complete
+      if (t == 8) {  // block i + 1's half is complete
+        store_partial(own, n0);
+        s_own = n0;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -345,8 +345,11 @@ __device__ __forceinline__ void write_rows(const SplitArgs& a, const WaveState& 
     const float inv_i = __shfl(inv, r, 64);
     if (m_slice + r < M) {
       float* rowp = base + (size_t)r * kNope + col;
+      // streaming stores: the outputs are not read again by this kernel, and dirty
+      // lines left in L2 would be written back at the kernel boundary
 #pragma unroll
-      for (int ct = 0; ct < kColTilesPerWave; ++ct) rowp[32 * ct] = ws.acc[ct][i] * inv_i;
+      for (int ct = 0; ct < kColTilesPerWave; ++ct)
+        __builtin_nontemporal_store(ws.acc[ct][i] * inv_i, rowp + 32 * ct);
     }
   }
   if (c == 0 && lane < 32 && m_slice + lane < M) {
@@ -490,7 +493,11 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     else
       wait_vmem_all();
     __syncthreads();  // block 0 is in LDS
-    if (nb > 0) store_partial(own, qk_partial(ring_slot(ring, 0), rb, qreg));
+    f32x16 s_own = {};  // this wave's half of S^T of the block being scored
+    if (nb > 0) {
+      s_own = qk_partial(ring_slot(ring, 0), rb, qreg);
+      store_partial(own, s_own);
+    }
     int i = 0;
     for (; i + 1 < nb; ++i) {
       // block i + 1 has landed ...  (at least one step's copies were issued after
@@ -512,16 +519,16 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
         else
           stage_block(src_new, ring_slot(ring, i + 3), valid, so);
       }
-      pipe_step<true>(ring_slot(ring, i), ring_slot(ring, i + 1), rb, qreg, own, partner, ws,
-                      lim_of(i), a.scale_log2, job, so);
+      pipe_step<true>(ring_slot(ring, i), ring_slot(ring, i + 1), rb, qreg, s_own, own, partner,
+                      ws, lim_of(i), a.scale_log2, job, so);
       src_cur = src_next;
       src_next = src_ahead;
       src_ahead = src_new;
     }
     if (i < nb) {  // the last block (already in LDS): nothing left to score ahead or copy
       __syncthreads();
-      pipe_step<false>(ring_slot(ring, i), nullptr, rb, qreg, own, partner, ws, lim_of(i),
-                       a.scale_log2, CopyJob{}, so);
+      pipe_step<false>(ring_slot(ring, i), nullptr, rb, qreg, s_own, own, partner, ws,
+                       lim_of(i), a.scale_log2, CopyJob{}, so);
     }
     // a row whose scores outgrew its reference by more than the lazy bound forces a
     // second pass for the whole workgroup; the flag lives in the exchange buffer
