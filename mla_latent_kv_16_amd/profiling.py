@@ -3,6 +3,7 @@
     python -m mla_latent_kv_16_amd.profiling stats   <kernel_stats.csv> <out.md> "<command>"
     python -m mla_latent_kv_16_amd.profiling traffic <fetch_counter.csv> <write_counter.csv>
                                                      <workload> <out.json> "<commands>"
+    python -m mla_latent_kv_16_amd.profiling counters <out.md> "<commands>" <counter.csv>...
 
 `stats` keeps the per-kernel table of a `--kernel-trace --stats` run.  `traffic`
 turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of `bench.py --copy-probe`
@@ -24,7 +25,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/mla_kernels.hip", "csrc/mla_device.h", "csrc/mla_internal.h",
                   "csrc/mla_api.hip"]
 SPLIT_KERNEL = "splitkv_kernel"
-COMBINE_KERNEL = "combine_kernel"
+COMBINE_KERNEL = "combine"  # combine_kernel and combine_rows_kernel
 # bench.py --copy-probe copies this many bytes per launch (a plain device-to-device copy)
 COPY_PROBE_BYTES = 256 << 20
 
@@ -111,6 +112,22 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, commands: str) -> dic
     return res
 
 
+def counters_table(paths) -> str:
+    """Per-dispatch averages of every counter in the given --pmc CSVs, per kernel."""
+    per = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        for r in _rows(path):
+            per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = ["| kernel | counter | dispatches | average per dispatch |", "|---|---|---|---|"]
+    for k in sorted(per):
+        if "copy" in k.lower() or "elementwise" in k.lower():
+            continue
+        for c in sorted(per[k]):
+            v = per[k][c]
+            out.append(f"| `{k[:60]}` | {c} | {len(v)} | {sum(v) / len(v):.4g} |")
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         src, dst, cmd = argv[1], argv[2], argv[3]
@@ -124,6 +141,13 @@ def main(argv):
         with open(argv[4], "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res, indent=1))
+    elif len(argv) >= 4 and argv[0] == "counters":
+        dst, cmd = argv[1], argv[2]
+        with open(dst, "w") as f:
+            f.write(f"# Hardware counters\n\nCommands:\n\n```\n{cmd}\n```\n\n")
+            f.write(f"Kernel sources hash: `{kernel_hash()}`\n\n")
+            f.write(counters_table(argv[3:]) + "\n")
+        print(dst)
     else:
         print(__doc__)
         return 2
