@@ -13,8 +13,9 @@ read (every visible row once, 576 bf16) divided by the measured time per step.
 `roofline` rates the dominant kernel (the split-KV pass) against its MI355X peak.
 Its duration is measured with HIP events on the stream the kernels run on, around
 a run of back-to-back split launches over the same pool rotation after the timed
-steps (per-launch events inside the steps are reported too; they also count each
-launch's dispatch and end-of-kernel release).  Its `traffic` is the HBM bytes per
+steps.  Per-launch split durations (from a separate run of the steps with an event
+pair around each split launch) are reported too; they also count each launch's
+dispatch and end-of-kernel release.  Its `traffic` is the HBM bytes per
 launch measured by rocprofv3 counters (stored under profiles/ and used only while
 the kernel sources are unchanged).  `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
@@ -173,20 +174,29 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # The library launches on torch's current stream, where these events are recorded.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # The timed steps: nothing but the decode calls between the two synchronisations.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    split_ms = [a.elapsed_time(b) for a, b in evs]
-    split_avg = float(np.mean(split_ms))
     if mla.read_error_flags(ws):
         raise SystemExit("kernel reported a data fault flag")
+
+    # Per-launch split durations, from a second run of the same steps with events
+    # around each split launch.  The library launches on torch's current stream, where
+    # these events are recorded.  An event adds a marker to the stream, so this run is
+    # kept out of the timed steps.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    split_ms = [a.elapsed_time(b) for a, b in evs]
+    split_avg = float(np.mean(split_ms))
 
     # The dominant kernel alone: the split pass launched back to back over the same
     # rotation of pools, two events around the whole run.  Per-launch events around
