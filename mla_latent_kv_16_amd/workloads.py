@@ -28,6 +28,10 @@ Recipe (numpy PCG64, seed per workload), in this order:
   5. q_rope standard_normal([B, Sq, H, 64]) * q_sigma -> bf16.
 Pool pages no request uses, and the rows past L_b in each request's last page,
 hold bf16 quiet NaN (0x7FC0) so any stray read shows up in the result.
+
+FP8 latent pools (kv_format="e4m3"): the same draws, divided by a per-tensor
+scale and rounded to OCP FP8 E4M3 (round-to-nearest-even, saturating at +-448);
+kv_pool is then uint8 [P, 64, 576] and stray rows hold the E4M3 NaN code 0x7F.
 """
 from __future__ import annotations
 
@@ -42,6 +46,9 @@ D_R = 64           # decoupled RoPE key width
 D_ROW = D_C + D_R  # one pool row
 PAGE = 64          # rows per page
 BF16_NAN = np.uint16(0x7FC0)
+E4M3_NAN = np.uint8(0x7F)
+E4M3_MAX = 448.0
+DEFAULT_KV_SCALE = 2.0 ** -6  # N(0,1) latents / 2^-6 stay inside +-448
 DEFAULT_SCALE = np.float32(192.0 ** -0.5)  # (128 nope + 64 rope) ** -0.5
 
 
@@ -93,16 +100,42 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r
 
 
+def _e4m3_positive_values() -> np.ndarray:
+    """The 127 non-negative finite E4M3 values, indexed by code 0x00..0x7E."""
+    c = np.arange(127)
+    e, m = c >> 3, (c & 7).astype(np.float64)
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+
+
+_E4M3_POS = _e4m3_positive_values()
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to OCP FP8 E4M3 codes: nearest value, ties to the
+    even code, magnitudes beyond 448 saturated to 448.  Returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x).astype(np.float64), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+
+
 @dataclasses.dataclass
 class Workload:
     spec: WorkloadSpec
     q_nope: np.ndarray       # uint16 [B, Sq, H, 512]
     q_rope: np.ndarray       # uint16 [B, Sq, H, 64]
-    kv_pool: np.ndarray      # uint16 [P, 64, 576]
+    kv_pool: np.ndarray      # uint16 bf16 bits, or uint8 E4M3 codes [P, 64, 576]
     block_table: np.ndarray  # int32 [B, max_pages]
     seq_lens: np.ndarray     # int32 [B]
     scale: np.float32
     causal: bool
+    kv_format: str = "bf16"  # "bf16" or "e4m3"
+    kv_scale: float = 1.0    # per-tensor dequantization scale of an E4M3 pool
 
     @property
     def B(self):
@@ -124,9 +157,13 @@ class Workload:
     def max_pages(self):
         return self.block_table.shape[1]
 
+    @property
+    def row_bytes(self) -> int:
+        return D_ROW * (1 if self.kv_format == "e4m3" else 2)
+
     def kv_bytes(self) -> int:
-        """Latent bytes a step must read: every visible row once, 576 bf16 each."""
-        return int(self.seq_lens.astype(np.int64).sum()) * D_ROW * 2
+        """Latent bytes a step must read: every visible row once (576 bf16 or E4M3)."""
+        return int(self.seq_lens.astype(np.int64).sum()) * self.row_bytes
 
 
 def _draw_lens(spec: WorkloadSpec, rng: np.random.Generator, B: int) -> np.ndarray:
@@ -143,8 +180,14 @@ def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] 
                   lens=None, causal: Optional[bool] = None,
                   q_sigma: Optional[float] = None, kv_sigma: Optional[float] = None,
                   poison: bool = True, pool_factor: int = 2,
-                  scale: Optional[float] = None) -> Workload:
-    """Build one seeded workload.  Any keyword overrides the named spec."""
+                  scale: Optional[float] = None, kv_format: str = "bf16",
+                  kv_scale: Optional[float] = None) -> Workload:
+    """Build one seeded workload.  Any keyword overrides the named spec.  With
+    kv_format="e4m3" the latent rows are the same draws stored as E4M3 codes of
+    value / kv_scale."""
+    if kv_format not in ("bf16", "e4m3"):
+        raise ValueError(kv_format)
+    kvs = float(DEFAULT_KV_SCALE if kv_scale is None else kv_scale)
     spec = WORKLOADS[spec_or_name] if isinstance(spec_or_name, str) else spec_or_name
     over = {k: v for k, v in dict(seed=seed, B=B, Sq=Sq, H=H, lens=lens, causal=causal,
                                   q_sigma=q_sigma, kv_sigma=kv_sigma).items() if v is not None}
@@ -167,12 +210,20 @@ def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] 
         block_table[b, :n] = perm[off:off + n]
         off += n
 
-    fill = BF16_NAN if poison else np.uint16(0)
-    pool = np.full((pool_pages, PAGE, D_ROW), fill, dtype=np.uint16)
+    if kv_format == "e4m3":
+        fill = E4M3_NAN if poison else np.uint8(0)
+        pool = np.full((pool_pages, PAGE, D_ROW), fill, dtype=np.uint8)
+    else:
+        fill = BF16_NAN if poison else np.uint16(0)
+        pool = np.full((pool_pages, PAGE, D_ROW), fill, dtype=np.uint16)
     for b in range(Bn):
         Lb = int(L[b])
-        rows = f32_to_bf16_bits(rng.standard_normal((Lb, D_ROW), dtype=np.float32)
-                                * np.float32(spec.kv_sigma))
+        draws = rng.standard_normal((Lb, D_ROW), dtype=np.float32) * np.float32(spec.kv_sigma)
+        if kv_format == "e4m3":
+            rows = f32_to_e4m3_bits(draws / np.float32(kvs))
+        else:
+            rows = f32_to_bf16_bits(draws)
+        del draws
         n = int(pages_per[b])
         full = Lb // PAGE
         if full:
@@ -188,7 +239,7 @@ def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] 
                               * np.float32(spec.q_sigma))
     sc = DEFAULT_SCALE if scale is None else np.float32(scale)
     return Workload(spec, q_nope, q_rope, pool, block_table, L.astype(np.int32), sc,
-                    bool(spec.causal))
+                    bool(spec.causal), kv_format, kvs if kv_format == "e4m3" else 1.0)
 
 
 def kv_bytes_expected(spec: WorkloadSpec) -> float:

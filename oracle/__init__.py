@@ -6,6 +6,8 @@ calls the HIP library.
 """
 from .mla_oracle import (  # noqa: F401
     bf16_bits_to_f64,
+    e4m3_bits_to_f64,
+    E4M3Pool,
     gather_latent_rows,
     visible_rows,
     mla_attention_loop,

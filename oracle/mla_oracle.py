@@ -69,6 +69,38 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode OCP FP8 E4M3 (E4M3FN) bit patterns (uint8) to float64 exactly.
+
+    Sign bit, 4 exponent bits with bias 7, 3 mantissa bits.  Exponent field 0 holds
+    the subnormals m/8 * 2^-6; the all-ones exponent with all-ones mantissa is NaN
+    and there is no infinity, so the largest finite value is 1.75 * 2^8 = 448.
+    """
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, out)
+
+
+class E4M3Pool:
+    """A latent pool stored as E4M3 codes with one per-tensor scale, read as float64.
+
+    Indexing returns the dequantized rows (code value * scale, exact in float64), so
+    the gather below reads it like any float pool.
+    """
+
+    def __init__(self, codes: np.ndarray, scale: float):
+        self.codes = np.asarray(codes, dtype=np.uint8)
+        self.scale = float(scale)
+        self.shape = self.codes.shape
+
+    def __getitem__(self, idx):
+        return e4m3_bits_to_f64(self.codes[idx]) * self.scale
+
+
 def _f64(x) -> np.ndarray:
     """bf16 bit patterns (uint16) are widened exactly; any float array is taken as is.
 
