@@ -43,15 +43,15 @@ def log(*a):
 def algorithmic_work(w):
     """Bytes a step must move and flops it must do (split partials not counted).
 
-    Bytes: every visible latent row once (576 bf16), the queries (576 bf16 per
-    folded row), the outputs (512 fp32 + 1 fp32 LSE per folded row) and the block
-    table entries of the visible pages.  Flops: 2 (576 + 512) per visible
-    (query row, key) pair."""
+    Bytes: every visible latent row once (576 values: bf16, or E4M3 for an E4M3
+    pool), the queries (576 bf16 per folded row), the outputs (512 fp32 + 1 fp32 LSE
+    per folded row) and the block table entries of the visible pages.  Flops:
+    2 (576 + 512) per visible (query row, key) pair."""
     import numpy as np
     L = w.seq_lens.astype(np.int64)
     M = w.Sq * w.H
     pages = int(((L + 63) // 64).sum())
-    kv = int(L.sum()) * 1152
+    kv = w.kv_bytes()
     q = w.B * M * 1152
     out = w.B * M * (512 * 4 + 4)
     bt = pages * 4
@@ -67,20 +67,21 @@ def algorithmic_work(w):
 def cpu_baseline(w, budget_s=12.0):
     """fp64 oracle on whole requests (cycling through the batch) until ~budget_s has
     passed; KV bytes of the requests done over the wall time, in GB/s."""
-    from oracle import mla_attention_folded
+    from oracle import E4M3Pool, mla_attention_folded
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    pool = E4M3Pool(w.kv_pool, w.kv_scale) if w.kv_format == "e4m3" else w.kv_pool
     done, kv, t0 = 0, 0, time.perf_counter()
     while True:
         b = done % w.B
         sl = slice(b, b + 1)
-        mla_attention_folded(w.q_nope[sl], w.q_rope[sl], w.kv_pool, w.block_table[sl],
+        mla_attention_folded(w.q_nope[sl], w.q_rope[sl], pool, w.block_table[sl],
                              w.seq_lens[sl], w.scale, w.causal)
         done += 1
-        kv += int(w.seq_lens[b]) * 1152
+        kv += int(w.seq_lens[b]) * w.row_bytes
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
@@ -90,11 +91,12 @@ def cpu_baseline(w, budget_s=12.0):
             "seconds_per_step_extrapolated": dt * w.B / done}
 
 
-def stored_traffic(config):
-    """HBM bytes per split-KV launch from profiles/traffic_<config>.json, if the
-    counters were taken on the current kernel sources."""
+def stored_traffic(config, kv):
+    """HBM bytes per split-KV launch from profiles/traffic_<config>[_e4m3].json, if
+    the counters were taken on the current kernel sources."""
     from mla_latent_kv_16_amd.profiling import kernel_hash
-    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    tag = config if kv == "bf16" else f"{config}_{kv}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -114,6 +116,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="spec4",
                     help="tiny | spec4 | spec8 | spec16 | sweep | prefill")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "e4m3"],
+                    help="latent pool format: bf16, or E4M3 codes with a per-tensor scale")
     ap.add_argument("--partitions", type=int, default=0, help="0 = library default")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies cycled per step (0 = enough to exceed 2x MALL)")
@@ -137,9 +141,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    w = make_workload(args.config)
+    w = make_workload(args.config, kv_format=args.kv)
     work = algorithmic_work(w)
-    log(f"{args.config}: B={w.B} Sq={w.Sq} H={w.H} pages={work['pages']} "
+    log(f"{args.config} ({args.kv} pool): B={w.B} Sq={w.Sq} H={w.H} pages={work['pages']} "
         f"kv={work['kv_bytes'] / 1e6:.1f} MB, generated in {time.perf_counter() - t_gen:.1f}s")
 
     # Cycle over independent copies of the pool so that consecutive steps cannot be
@@ -148,7 +152,12 @@ def main():
     n_copies = args.rotate or max(1, min(4, int(np.ceil(2 * 256e6 / max(work["kv_bytes"], 1))) + 1))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
     q_nope, q_rope = t(w.q_nope), t(w.q_rope)
-    pools = [t(w.kv_pool) for _ in range(n_copies)]
+    if args.kv == "e4m3":
+        pools = [torch.from_numpy(w.kv_pool).to(dev) for _ in range(n_copies)]
+        kv_scale = w.kv_scale
+    else:
+        pools = [t(w.kv_pool) for _ in range(n_copies)]
+        kv_scale = None
     bt = torch.from_numpy(w.block_table).to(dev)
     sl = torch.from_numpy(w.seq_lens).to(dev)
     G = args.partitions or mla.auto_partitions(w.B, w.Sq, w.H, w.max_pages)
@@ -158,8 +167,8 @@ def main():
     scale = float(w.scale)
     log(f"partitions={G} pool copies={n_copies} ({pool_bytes / 1e9:.2f} GB each)")
 
-    calls = [mla.BoundDecode(q_nope, q_rope, pool, bt, sl, scale, w.causal, G, O, lse, ws)
-             for pool in pools]
+    calls = [mla.BoundDecode(q_nope, q_rope, pool, bt, sl, scale, w.causal, G, O, lse, ws,
+                             kv_scale=kv_scale) for pool in pools]
 
     def step(i, ev=None):
         c = calls[i % n_copies]
@@ -223,8 +232,10 @@ def main():
     value = work["kv_bytes"] / (ms_step * 1e-3) / 1e9
     hbm_achieved = work["bytes"] / (split_b2b * 1e-3) / 1e9
     mfma_achieved = work["flops"] / (split_b2b * 1e-3) / 1e12
-    traffic = stored_traffic(args.config)
-    mfma_bound = args.config in ("prefill", "spec16")
+    traffic = stored_traffic(args.config, args.kv)
+    # the bound is the roof the step's arithmetic intensity meets first
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    mfma_bound = work["flops"] / work["bytes"] > ridge
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(mfma_achieved, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -258,10 +269,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 latents and queries; pages scattered in a 2x pool)",
+        "data": ("synthetic (seeded N(0,1) latents and queries; pages scattered in a 2x pool"
+                 + (f"; latents stored as E4M3 codes of value / {w.kv_scale})" if args.kv == "e4m3"
+                    else ")")),
         "config": {"workload": args.config, "B": w.B, "Sq": w.Sq, "H": w.H,
                    "context": [int(w.seq_lens.min()), int(w.seq_lens.max())],
-                   "page_size": 64, "latent": "512+64 bf16", "partitions": G,
+                   "page_size": 64,
+                   "latent": "512+64 " + ("e4m3, per-tensor scale" if args.kv == "e4m3"
+                                          else "bf16"),
+                   "partitions": G,
                    "kv_bytes": work["kv_bytes"], "tflops_per_step": work["flops"] / 1e12},
         "kv_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "split_pass_us": round(split_avg * 1e3, 2),

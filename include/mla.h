@@ -155,6 +155,34 @@ int mla_prefill_with_prefix(const uint16_t* q_nope, const uint16_t* q_rope,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same decode over an FP8 latent pool ("Faster kernels, slower engine", section
+ * "Three server boots, not one universal configuration": the MI355X serving runs
+ * keep the KV cache in fp8, which halves the bytes moved per cached token).
+ *
+ *   kv_pool   OCP FP8 E4M3 codes (E4M3FN: bias 7, no infinity, 0x7F/0xFF NaN),
+ *             uint8 [num_pages, 64, 576], rows [c_kv 0..511 | k_rope 512..575],
+ *             16-byte aligned
+ *   kv_scale  per-tensor dequantization scale: a row element is code_value * kv_scale;
+ *             must be finite and > 0 (else MLA_ERR_INVALID_ARG)
+ *
+ * Every other argument, the workspace and the outputs are as for mla_decode /
+ * mla_decode_splitkv; the combine pass is mla_decode_combine.  The scores and P V
+ * run in bf16 on the exact widening of the codes (every E4M3 value is a bf16 value),
+ * with kv_scale folded into the softmax scale and into O.
+ */
+int mla_decode_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* kv_pool,
+                    float kv_scale, int64_t num_pages, int page_size,
+                    const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+                    int B, int Sq, int H, float softmax_scale, int causal, int num_partitions,
+                    float* O, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+int mla_decode_splitkv_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
+                            const uint8_t* kv_pool, float kv_scale, int64_t num_pages,
+                            int page_size, const int32_t* block_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                            int causal, int num_partitions, float* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Waits for `stream`, then copies the workspace header's error flags
  * (MLA_FLAG_*) to *flags and clears them.  Reading forces a synchronisation, so
  * callers use it in checked runs and tests, not on the hot path.

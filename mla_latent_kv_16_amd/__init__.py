@@ -12,7 +12,9 @@ from ._binding import (  # noqa: F401
     auto_partitions,
     decode,
     decode_combine,
+    decode_e4m3,
     decode_splitkv,
+    decode_splitkv_e4m3,
     header_functions,
     lib,
     new_workspace,

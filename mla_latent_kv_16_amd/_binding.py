@@ -36,6 +36,8 @@ _sz = ctypes.c_size_t
 
 _COMPUTE_ARGS = [_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _i32,
                  _vp, _vp, _vp, _sz, _vp]
+_COMPUTE_ARGS_E4M3 = [_vp, _vp, _vp, _f32, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                      _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 _SIGNATURES = {
     "mla_status_string": ([_i32], ctypes.c_char_p),
     "mla_decode_auto_partitions": ([_i32, _i32, _i32, _i32, ctypes.POINTER(_i32)], _i32),
@@ -43,6 +45,8 @@ _SIGNATURES = {
     "mla_decode": (_COMPUTE_ARGS, _i32),
     "mla_decode_splitkv": (_COMPUTE_ARGS, _i32),
     "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
+    "mla_decode_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
+    "mla_decode_splitkv_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_combine": ([_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_read_error_flags": ([_vp, _vp, ctypes.POINTER(ctypes.c_uint32)], _i32),
 }
@@ -138,7 +142,8 @@ def new_workspace(B, Sq, H, max_pages_per_seq, num_partitions=0, device=None):
     return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
 
 
-def _prep(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace, num_partitions):
+def _prep(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace, num_partitions,
+          e4m3=False):
     torch = _torch()
     bf = (torch.bfloat16, torch.int16)
     if q_nope.dim() != 4:
@@ -150,7 +155,7 @@ def _prep(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace, n
     _expect(q_rope, "q_rope", bf, (B, Sq, H, ROPE_DIM))
     if kv_pool.dim() != 3 or kv_pool.shape[1] != PAGE_SIZE or kv_pool.shape[2] != NOPE_DIM + ROPE_DIM:
         raise ValueError("kv_pool must be [num_pages, 64, 576]")
-    _expect(kv_pool, "kv_pool", bf)
+    _expect(kv_pool, "kv_pool", (torch.uint8,) if e4m3 else bf)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_pages_per_seq]")
     _expect(block_table, "block_table", (torch.int32,))
@@ -180,6 +185,37 @@ def _compute(fn_name, q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_sc
             workspace.numel(), _stream_handle(stream))
     _check(st, fn_name)
     return out, lse
+
+
+def _compute_e4m3(fn_name, q_nope, q_rope, kv_pool, kv_scale, block_table, seq_lens,
+                  softmax_scale, causal, num_partitions, out, lse, workspace, stream):
+    B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table, seq_lens,
+                                                out, lse, workspace, num_partitions, e4m3=True)
+    fn = getattr(lib(), fn_name)
+    st = fn(_ptr(q_nope), _ptr(q_rope), _ptr(kv_pool), float(kv_scale), kv_pool.shape[0],
+            PAGE_SIZE, _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H, float(softmax_scale),
+            1 if causal else 0, int(num_partitions), _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel(), _stream_handle(stream))
+    _check(st, fn_name)
+    return out, lse
+
+
+def decode_e4m3(q_nope, q_rope, kv_pool, kv_scale, block_table, seq_lens, softmax_scale,
+                causal=True, num_partitions=0, out=None, lse=None, workspace=None, stream=None):
+    """mla_decode_e4m3: decode over an E4M3 pool (uint8 [P, 64, 576]) with a per-tensor
+    scale.  Returns (O fp32 [B,Sq,H,512], lse fp32 [B,Sq,H])."""
+    return _compute_e4m3("mla_decode_e4m3", q_nope, q_rope, kv_pool, kv_scale, block_table,
+                         seq_lens, softmax_scale, causal, num_partitions, out, lse, workspace,
+                         stream)
+
+
+def decode_splitkv_e4m3(q_nope, q_rope, kv_pool, kv_scale, block_table, seq_lens,
+                        softmax_scale, causal=True, num_partitions=0, out=None, lse=None,
+                        workspace=None, stream=None):
+    """mla_decode_splitkv_e4m3: the split-KV pass alone over an E4M3 pool."""
+    return _compute_e4m3("mla_decode_splitkv_e4m3", q_nope, q_rope, kv_pool, kv_scale,
+                         block_table, seq_lens, softmax_scale, causal, num_partitions, out, lse,
+                         workspace, stream)
 
 
 def decode(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
@@ -232,20 +268,28 @@ class BoundDecode:
     """
 
     def __init__(self, q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
-                 num_partitions=0, out=None, lse=None, workspace=None, stream=None):
+                 num_partitions=0, out=None, lse=None, workspace=None, stream=None,
+                 kv_scale=None):
+        e4m3 = kv_scale is not None  # an E4M3 pool comes with its scale
         B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table,
-                                                    seq_lens, out, lse, workspace, num_partitions)
+                                                    seq_lens, out, lse, workspace, num_partitions,
+                                                    e4m3=e4m3)
         self.tensors = (q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace)
         self.out, self.lse, self.workspace = out, lse, workspace
         self.num_partitions = int(num_partitions) or auto_partitions(B, Sq, H, maxp)
-        self._args = (_ptr(q_nope), _ptr(q_rope), _ptr(kv_pool), kv_pool.shape[0], PAGE_SIZE,
+        pool_args = ((_ptr(kv_pool), float(kv_scale)) if e4m3 else (_ptr(kv_pool),))
+        self._args = (_ptr(q_nope), _ptr(q_rope), *pool_args, kv_pool.shape[0], PAGE_SIZE,
                       _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H, float(softmax_scale),
                       1 if causal else 0, self.num_partitions, _ptr(out), _ptr(lse),
                       _ptr(workspace), workspace.numel(), _stream_handle(stream))
         self._cargs = (_ptr(seq_lens), maxp, B, Sq, H, self.num_partitions, _ptr(out), _ptr(lse),
                        _ptr(workspace), workspace.numel(), _stream_handle(stream))
         L = lib()
-        self._decode, self._split, self._combine = L.mla_decode, L.mla_decode_splitkv, L.mla_decode_combine
+        if e4m3:
+            self._decode, self._split = L.mla_decode_e4m3, L.mla_decode_splitkv_e4m3
+        else:
+            self._decode, self._split = L.mla_decode, L.mla_decode_splitkv
+        self._combine = L.mla_decode_combine
 
     def __call__(self):
         _check(self._decode(*self._args), "mla_decode")

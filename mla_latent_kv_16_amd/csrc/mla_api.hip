@@ -109,7 +109,7 @@ struct Call {
 };
 
 // Shared checks of every compute entry point.
-int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool,
             int64_t num_pages, int page_size, const int32_t* block_table, int max_pages,
             const int32_t* seq_lens, int B, int Sq, int H, float scale, int causal,
             int num_partitions, const float* O, const float* lse, void* ws, size_t ws_bytes,
@@ -137,9 +137,10 @@ int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_p
 }
 
 int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
-                  const uint16_t* kv_pool, int64_t num_pages, const int32_t* block_table,
-                  int max_pages, const int32_t* seq_lens, int B, int Sq, int H, float scale,
-                  int causal, float* O, float* lse, hipStream_t stream) {
+                  const void* kv_pool, int kv_e4m3, float kv_scale, int64_t num_pages,
+                  const int32_t* block_table, int max_pages, const int32_t* seq_lens, int B,
+                  int Sq, int H, float scale, int causal, float* O, float* lse,
+                  hipStream_t stream) {
   SplitArgs a;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
@@ -161,7 +162,9 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
   a.G = c.G;
   a.slot_rows = c.geo.slot_rows;
   a.causal = causal;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.kv_e4m3 = kv_e4m3;
+  a.kv_scale = kv_scale;
+  a.scale_log2 = scale * kv_scale * 1.4426950408889634f;
   return launch_splitkv(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -233,8 +236,8 @@ int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uin
                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
-  return enqueue_split(c, q_nope, q_rope, kv_pool, num_pages, block_table, max_pages_per_seq,
-                       seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
+  return enqueue_split(c, q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, block_table,
+                       max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -266,8 +269,8 @@ int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* k
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = enqueue_split(c, q_nope, q_rope, kv_pool, num_pages, block_table, max_pages_per_seq,
-                     seq_lens, B, Sq, H, softmax_scale, causal, O, lse, s);
+  st = enqueue_split(c, q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse, s);
   if (st != MLA_OK) return st;
   return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
 }
@@ -281,6 +284,41 @@ int mla_prefill_with_prefix(const uint16_t* q_nope, const uint16_t* q_rope,
   return mla_decode(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
                     seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                     workspace_bytes, stream);
+}
+
+int mla_decode_splitkv_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
+                            const uint8_t* kv_pool, float kv_scale, int64_t num_pages,
+                            int page_size, const int32_t* block_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                            int causal, int num_partitions, float* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(kv_scale > 0.0f) || isinf(kv_scale)) return MLA_ERR_INVALID_ARG;
+  Call c;
+  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                   workspace_bytes, &c);
+  if (st != MLA_OK) return st;
+  return enqueue_split(c, q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, block_table,
+                       max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
+                       static_cast<hipStream_t>(stream));
+}
+
+int mla_decode_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* kv_pool,
+                    float kv_scale, int64_t num_pages, int page_size, const int32_t* block_table,
+                    int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
+                    float softmax_scale, int causal, int num_partitions, float* O, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(kv_scale > 0.0f) || isinf(kv_scale)) return MLA_ERR_INVALID_ARG;
+  Call c;
+  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                   workspace_bytes, &c);
+  if (st != MLA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = enqueue_split(c, q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse, s);
+  if (st != MLA_OK) return st;
+  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
 }
 
 int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {

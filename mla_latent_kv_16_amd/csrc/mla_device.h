@@ -37,9 +37,24 @@ constexpr int kStages = 4;                         // LDS ring depth (two blocks
 constexpr int kStageCopiesPerWave = 9;             // 16-byte-per-lane copies per wave per block
 constexpr int kCombineThreads = 256;
 
+// E4M3 latent pools (one byte per element): a row is 576 bytes, a page 36,864 and a
+// 32-row block 18,432 = 1,152 sixteen-byte chunks.  Each wave copies 5 KB of a block
+// (4 x 5 KB = the block plus 2 KB of padding at the end of its slot), and the ring
+// has six slots, so four blocks are in flight while two are being scored.
+constexpr int kRowBytes8 = kRow;                               // 576
+constexpr int kPageBytes8 = kPage * kRowBytes8;                // 36,864
+constexpr int kChunks8 = kRowBytes8 / 16;                      // 36
+constexpr int kBlockBytes8 = kKvBlock * kRowBytes8;            // 18,432
+constexpr int kBlockChunks8 = kBlockBytes8 / 16;               // 1,152
+constexpr int kStageCopies8 = 5;                               // 1 KB copies per wave per block
+constexpr int kSlotBytes8 = kWaves * kStageCopies8 * 1024;     // 20,480
+constexpr int kStages8 = 6;
+constexpr int kKSteps8 = kQStepsPerWave / 2;                   // 9 sixteen-byte K reads per wave
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -57,6 +72,16 @@ __device__ __forceinline__ int swz(int r) {
   return ((i & 1) << 2) | (i & 2) | ((i >> 2) & 1);  // 3-bit bit reversal
 }
 
+// E4M3 rows: 16-byte chunk c of row r sits at chunk position c ^ swz8(r).  The xor
+// only touches the low two chunk bits (a row's 36 chunks are nine aligned groups of
+// four).  With 576-byte rows (9 x 64 bytes) the bank of a chunk repeats every four
+// rows; swz8 takes bits 2 and 3 of the row so that the sixteen-byte K reads of 16
+// consecutive rows and the transposed V reads (8 rows x 2 chunks per 32 lanes) hit
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz8(int r) {
+  return ((r >> 2) & 1) | ((((r >> 3) ^ (r >> 2)) & 1) << 1);
+}
+
 // ---- instruction wrappers ---------------------------------------------------
 // 32x32x16 bf16 MFMA.  A [32 x 16]: lane l holds row l % 32, k = 8 (l / 32) + 0..7.
 // B [16 x 32]: lane l holds column l % 32, the same k.  D [32 x 32]: lane l holds
@@ -68,6 +93,9 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 __device__ __forceinline__ bf16x8 lds_read_b128(const uint8_t* lds_base, int byte_off) {
   return *reinterpret_cast<const bf16x8*>(lds_base + byte_off);
 }
+__device__ __forceinline__ u32x4 lds_read_u128(const uint8_t* lds_base, int byte_off) {
+  return *reinterpret_cast<const u32x4*>(lds_base + byte_off);
+}
 
 // LDS transpose read (gfx950): within each group of 16 lanes, when lane 4 r + c
 // addresses the 8-byte word at columns [4 c, 4 c + 4) of row r (r, c = 0..3), lane n
@@ -75,6 +103,26 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const uint8_t* lds_base, int byt
 // needs from a row-major tile.
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* lds_base, int byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(lds_base + byte_off));
+}
+
+// LDS transpose read of 8-bit data (gfx950): within each group of 16 lanes, lane n
+// receives byte n % 8 of the 8-byte words addressed by lanes 2 j + n / 8, j = 0..7.
+// When lane 2 j + e addresses columns [8 e, 8 e + 8) of row j, lane n gets column n
+// of rows 0..7: eight consecutive k of one column, as an MFMA operand wants them.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* lds_base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(lds_base + byte_off));
+}
+
+// Eight E4M3 codes (bytes 0..7 of w0, w1) to eight bf16 values, exactly: every E4M3
+// value is a bf16 value (scale factor 1).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 // LDS byte address of a pointer into __shared__ memory.

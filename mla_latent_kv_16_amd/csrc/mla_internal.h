@@ -10,7 +10,7 @@ namespace mla {
 struct SplitArgs {
   const uint16_t* q_nope;      // [B, M, 512] bf16, M = Sq * H folded rows (m = t * H + h)
   const uint16_t* q_rope;      // [B, M, 64]
-  const uint16_t* kv_pool;     // [num_pages, 64, 576]
+  const void* kv_pool;         // [num_pages, 64, 576] bf16, or E4M3 codes when kv_e4m3
   const int32_t* block_table;  // [B, max_pages]
   const int32_t* seq_lens;     // [B]
   float* O;                    // [B, M, 512]
@@ -25,7 +25,9 @@ struct SplitArgs {
   int G;                       // KV partitions
   int slot_rows;               // min(M, M-tile rows)
   int causal;
-  float scale_log2;            // softmax_scale * log2(e)
+  int kv_e4m3;                 // 1: the pool holds E4M3 codes scaled by kv_scale
+  float kv_scale;              // dequantization scale of the pool (1 for bf16)
+  float scale_log2;            // softmax_scale * kv_scale * log2(e)
 };
 
 struct CombineArgs {

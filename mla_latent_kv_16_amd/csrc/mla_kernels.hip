@@ -104,6 +104,86 @@ __device__ __forceinline__ void stage_block(const uint8_t* src, uint8_t* slot, i
   }
 }
 
+// E4M3 blocks: wave w copies LDS chunk positions q = 320 w .. 320 w + 319 of its slot
+// (five copies of 64 lanes x 16 bytes); positions past the block's 1,152 chunks are
+// the slot's padding and re-read an in-block chunk.  LDS chunk q holds row q / 36,
+// chunk (q % 36) ^ swz8(row) of the block.
+struct StageOffsets8 {
+  uint32_t off[kStageCopies8];
+};
+
+__device__ __forceinline__ uint32_t stage_src8(uint32_t q, int valid) {
+  if (q >= (uint32_t)kBlockChunks8) q -= kBlockChunks8;  // padding
+  const uint32_t r = q / kChunks8;
+  const uint32_t pos = q - r * kChunks8;
+  const uint32_t rs = min(r, (uint32_t)(valid - 1));  // rows past the length re-read the last
+  return rs * kRowBytes8 + ((pos ^ swz8(r)) << 4);
+}
+
+__device__ __forceinline__ StageOffsets8 stage_offsets8() {
+  StageOffsets8 so;
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < kStageCopies8; ++k)
+    so.off[k] = stage_src8((kStageCopies8 * wave + k) * 64 + lane, kKvBlock);
+  return so;
+}
+
+__device__ __forceinline__ uint32_t stage_dst8(const uint8_t* slot) {
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return lds_addr(slot) + kStageCopies8 * 1024 * wave;
+}
+
+__device__ __forceinline__ void stage_block8(const uint8_t* src, uint8_t* slot, int valid,
+                                             const StageOffsets8& so) {
+  const uint32_t dst = stage_dst8(slot);
+  if (valid == kKvBlock) {
+#pragma unroll
+    for (int k = 0; k < kStageCopies8; ++k) dma16(src, so.off[k], dst + k * 1024);
+  } else {  // the request's last block
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < kStageCopies8; ++k)
+      dma16(src, stage_src8((kStageCopies8 * wave + k) * 64 + lane, valid), dst + k * 1024);
+  }
+}
+
+// E4M3 read bases.  K (A operand of S^T): the k order inside each pair of k-steps is
+// permuted so that one sixteen-byte read feeds two MFMAs: for the wave's read t
+// (0..8) lane half h holds k = 32 (9 c + t) + 16 h + 0..15, bytes 0..7 for k-step 2 t
+// and 8..15 for k-step 2 t + 1 (the queries are loaded in the same order).  That is
+// chunk 18 c + 2 t + h of row lane % 32.  V (B operand of P V): transposed 8-bit
+// reads, where byte j of lane n of a 16-lane group comes from lane 2 j + n / 8 of the
+// group.  Byte j must hold the kv row that P's element j stands for (16 ks + 4 h +
+// j % 4 + 8 (j / 4), the S^T accumulator order), so lane 16 g + m addresses row
+// 16 ks + 4 (g / 2) + 8 (m / 8) + (m / 2) % 4 at columns 256 c + 32 ct + 16 (g % 2) +
+// 8 (m % 2).
+struct ReadBases8 {
+  int k[2];  // read t: k[t % 2] + 64 (t / 2)
+  int v[2];  // column tile ct, k-step ks: v[ct % 2] + 64 (ct / 2) + 16 * 576 ks
+};
+
+__device__ __forceinline__ ReadBases8 read_bases8(int c) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  ReadBases8 rb;
+  const int r = lane & 31, f = swz8(r);
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int C = 18 * c + 2 * v + h;
+    rb.k[v] = r * kRowBytes8 + (((C & ~3) | ((C & 3) ^ f)) << 4);
+  }
+  const int g = lane >> 4, m = lane & 15;
+  const int rv = 4 * (g >> 1) + 8 * (m >> 3) + ((m >> 1) & 3);
+  const int fv = swz8(rv);  // bits 2 and 3 of the row do not depend on ks
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int C = 16 * c + 2 * par + (g & 1);
+    rb.v[par] = rv * kRowBytes8 + (((C & ~3) | ((C & 3) ^ fv)) << 4) + 8 * (m & 1);
+  }
+  return rb;
+}
+
 // ---- per-lane LDS read bases ---------------------------------------------------
 // Every LDS address of the walk is (per-lane base) + (compile-time offset): the xor
 // swizzle touches only the low three chunk bits, so for each k-step or column tile
@@ -142,21 +222,169 @@ __device__ __forceinline__ ReadBases read_bases(int c) {
   return rb;
 }
 
+// ---- the two latent formats ------------------------------------------------------
+// Everything that depends on how a pool row is stored: bf16 (1,152-byte rows, 36 KB
+// blocks, a four-slot ring) or E4M3 with a per-tensor scale (576-byte rows, 18 KB
+// blocks in 20 KB slots, a six-slot ring).  The scores and P V run on bf16 MFMAs in
+// both cases: E4M3 operands are widened exactly in registers after the LDS read.
+struct Bf16Kv {
+  static constexpr int kStagesN = kStages;        // ring slots
+  static constexpr int kSlot = kStageBytes;       // bytes per slot
+  static constexpr int kCopies = kStageCopiesPerWave;
+  static constexpr int kPageB = kPageBytes;
+  static constexpr int kHalfB = kStageBytes;      // a 32-row block of a page
+  using Offsets = StageOffsets;
+  using Bases = ReadBases;
+  static __device__ __forceinline__ Offsets offsets() { return stage_offsets(); }
+  static __device__ __forceinline__ Bases bases(int c) { return read_bases(c); }
+  static __device__ __forceinline__ void stage(const uint8_t* src, uint8_t* slot, int valid,
+                                               const Offsets& so) {
+    stage_block(src, slot, valid, so);
+  }
+  static __device__ __forceinline__ uint32_t dst(const uint8_t* slot) {
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    return lds_addr(slot) + 8 * wave * kRowBytes;
+  }
+  // query element k of S^T k-step kk for lane half h (natural order)
+  static __device__ __forceinline__ int q_k(int c, int kk, int h) {
+    return (kQStepsPerWave * c + kk) * 16 + 8 * h;
+  }
+};
+
+struct E4m3Kv {
+  static constexpr int kStagesN = kStages8;
+  static constexpr int kSlot = kSlotBytes8;
+  static constexpr int kCopies = kStageCopies8;
+  static constexpr int kPageB = kPageBytes8;
+  static constexpr int kHalfB = kBlockBytes8;
+  using Offsets = StageOffsets8;
+  using Bases = ReadBases8;
+  static __device__ __forceinline__ Offsets offsets() { return stage_offsets8(); }
+  static __device__ __forceinline__ Bases bases(int c) { return read_bases8(c); }
+  static __device__ __forceinline__ void stage(const uint8_t* src, uint8_t* slot, int valid,
+                                               const Offsets& so) {
+    stage_block8(src, slot, valid, so);
+  }
+  static __device__ __forceinline__ uint32_t dst(const uint8_t* slot) { return stage_dst8(slot); }
+  // k order permuted inside each pair of k-steps (see read_bases8)
+  static __device__ __forceinline__ int q_k(int c, int kk, int h) {
+    return 32 * (kKSteps8 * c + (kk >> 1)) + 16 * h + 8 * (kk & 1);
+  }
+};
+
+// A-operand (K) stream of S^T for one block: operands for k-steps 0..17 in order,
+// with LDS reads running ahead of the MFMAs.
+template <class Kv> struct KStream;
+
+template <> struct KStream<Bf16Kv> {
+  static constexpr int DQ = 4;  // reads in flight
+  const uint8_t* blk;
+  const ReadBases* rb;
+  bf16x8 buf[DQ];
+  __device__ __forceinline__ bf16x8 rd(int kk) const {
+    return lds_read_b128(blk + rb->k[kk & 3], (kk >> 2) * 128);
+  }
+  __device__ __forceinline__ void start() {
+#pragma unroll
+    for (int u = 0; u < DQ; ++u) buf[u] = rd(u);
+  }
+  __device__ __forceinline__ bf16x8 next(int kk) {
+    const bf16x8 a = buf[kk % DQ];
+    if (kk + DQ < kQStepsPerWave) buf[kk % DQ] = rd(kk + DQ);
+    return a;
+  }
+};
+
+template <> struct KStream<E4m3Kv> {
+  const uint8_t* blk;
+  const ReadBases8* rb;
+  u32x4 raw[2];  // sixteen-byte reads t and t + 1 (each feeds two k-steps)
+  bf16x8 hi;     // the second k-step of the current read
+  __device__ __forceinline__ u32x4 rd(int t) const {
+    return lds_read_u128(blk + rb->k[t & 1], (t >> 1) * 64);
+  }
+  __device__ __forceinline__ void start() {
+    raw[0] = rd(0);
+    raw[1] = rd(1);
+  }
+  __device__ __forceinline__ bf16x8 next(int kk) {
+    if (kk & 1) return hi;
+    const int t = kk >> 1;
+    const u32x4 w = raw[t & 1];
+    if (t + 2 < kKSteps8) raw[t & 1] = rd(t + 2);
+    hi = e4m3x8_to_bf16(w[2], w[3]);
+    return e4m3x8_to_bf16(w[0], w[1]);
+  }
+};
+
+// B-operand (V) stream of O = P V for one block: operands for MFMA t = 8 ks + ct
+// (k-step ks of 16 kv rows, column tile ct of the wave's 256 columns).
+template <class Kv> struct VStream;
+
+template <> struct VStream<Bf16Kv> {
+  static constexpr int DV = 4;  // read pairs in flight
+  const uint8_t* blk;
+  const ReadBases* rb;
+  bf16x4 b0[DV], b1[DV];
+  __device__ __forceinline__ bf16x4 rd(int t, int sd) const {
+    const int ks = t >> 3, ct = t & 7;
+    return lds_read_tr(blk + rb->v[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
+  }
+  __device__ __forceinline__ void start() {
+#pragma unroll
+    for (int u = 0; u < DV; ++u) {
+      b0[u] = rd(u, 0);
+      b1[u] = rd(u, 1);
+    }
+  }
+  __device__ __forceinline__ bf16x8 next(int t) {
+    const int u = t % DV;
+    const bf16x8 v = {b0[u][0], b0[u][1], b0[u][2], b0[u][3],
+                      b1[u][0], b1[u][1], b1[u][2], b1[u][3]};
+    if (t + DV < 2 * kColTilesPerWave) {
+      b0[u] = rd(t + DV, 0);
+      b1[u] = rd(t + DV, 1);
+    }
+    return v;
+  }
+};
+
+template <> struct VStream<E4m3Kv> {
+  static constexpr int DV = 4;  // reads in flight
+  const uint8_t* blk;
+  const ReadBases8* rb;
+  i32x2 raw[DV];
+  __device__ __forceinline__ i32x2 rd(int t) const {
+    const int ks = t >> 3, ct = t & 7;
+    return lds_read_tr8(blk + rb->v[ct & 1], (ct >> 1) * 64 + ks * 16 * kRowBytes8);
+  }
+  __device__ __forceinline__ void start() {
+#pragma unroll
+    for (int u = 0; u < DV; ++u) raw[u] = rd(u);
+  }
+  __device__ __forceinline__ bf16x8 next(int t) {
+    const int u = t % DV;
+    const i32x2 w = raw[u];
+    if (t + DV < 2 * kColTilesPerWave) raw[u] = rd(t + DV);
+    return e4m3x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+  }
+};
+
 // ---- block copies issued from inside the pipeline step -------------------------
-// The vector memory path takes a wave's nine copies of a block only at its own pace
+// The vector memory path takes a wave's copies of a block only at its own pace
 // (hundreds of cycles), so the step issues them one per two S^T MFMAs instead of in
-// a burst at the top of the iteration.  A step always issues nine copies: when no
-// whole block is due, the job re-copies the block being scored into its own slot
-// (a whole block: only a request's last block can be partial, and it is never
+// a burst at the top of the iteration.  A step always issues one block's copies:
+// when no whole block is due, the job re-copies the block being scored into its own
+// slot (a whole block: only a request's last block can be partial, and it is never
 // scored ahead of another block), which writes the bytes already there.
 struct CopyJob {
   const uint8_t* src;  // first row of the block in the pool (wave-uniform)
-  uint32_t dst;        // LDS address of this wave's 8 rows in the block's slot
+  uint32_t dst;        // LDS address of this wave's share of the block's slot
 };
 
+template <class Kv>
 __device__ __forceinline__ CopyJob copy_job(const uint8_t* src, uint8_t* slot) {
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  return CopyJob{src, lds_addr(slot) + 8 * wave * kRowBytes};
+  return CopyJob{src, Kv::dst(slot)};
 }
 
 // ---- the software pipeline --------------------------------------------------------
@@ -171,18 +399,15 @@ __device__ __forceinline__ CopyJob copy_job(const uint8_t* src, uint8_t* slot) {
 // compiler neither serialises each read with its MFMA nor hoists everything to the top.
 
 // Own half of S^T for one staged block (the pipeline's first block).
-__device__ __forceinline__ f32x16 qk_partial(const uint8_t* blk, const ReadBases& rb,
+template <class Kv>
+__device__ __forceinline__ f32x16 qk_partial(const uint8_t* blk, const typename Kv::Bases& rb,
                                              const bf16x8* qreg) {
-  constexpr int DQ = 4;
-  auto qk_read = [&](int kk) { return lds_read_b128(blk + rb.k[kk & 3], (kk >> 2) * 128); };
+  KStream<Kv> ks{blk, &rb};
+  ks.start();
   f32x16 s0 = {};
-  bf16x8 abuf[DQ];
-#pragma unroll
-  for (int u = 0; u < DQ; ++u) abuf[u] = qk_read(u);
 #pragma unroll
   for (int kk = 0; kk < kQStepsPerWave; ++kk) {
-    s0 = mfma32(abuf[kk % DQ], qreg[kk], s0);
-    if (kk + DQ < kQStepsPerWave) abuf[kk % DQ] = qk_read(kk + DQ);
+    s0 = mfma32(ks.next(kk), qreg[kk], s0);
     __builtin_amdgcn_sched_barrier(0);
   }
   return s0;
@@ -198,48 +423,37 @@ __device__ __forceinline__ void store_partial(f32x4* xs, const f32x16& s) {
 // One iteration.  s_own is this wave's half of block i's S^T (kept in registers) and
 // `partner` the other wave's half in LDS.  When HAS_NEXT, this wave's half of block
 // i + 1 replaces s_own and its copy in `own` (read by the partner), after a
-// workgroup barrier that follows every wave's reads of block i's halves.  `lim` is the number of
-// leading rows of block i this lane's query row may see.
-template <bool HAS_NEXT>
+// workgroup barrier that follows every wave's reads of block i's halves.  `lim` is
+// the number of leading rows of block i this lane's query row may see.
+template <bool HAS_NEXT, class Kv>
 __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk_next,
-                                          const ReadBases& rb, const bf16x8* qreg,
+                                          const typename Kv::Bases& rb, const bf16x8* qreg,
                                           f32x16& s_own, f32x4* own, const f32x4* partner,
                                           WaveState& ws, int lim, float scale_log2,
-                                          const CopyJob& job, const StageOffsets& so) {
+                                          const CopyJob& job, const typename Kv::Offsets& so) {
   const int lane = threadIdx.x & 63;
-  constexpr int DQ = 4;                      // A-operand reads in flight
-  constexpr int DV = 4;                      // V-operand read pairs in flight
   constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
-  auto qk_read = [&](int kk) { return lds_read_b128(blk_next + rb.k[kk & 3], (kk >> 2) * 128); };
-  // t = 8 ks + ct, ks-major so consecutive MFMAs use different accumulators
-  auto pv_read = [&](int t, int sd) {
-    const int ks = t >> 3, ct = t & 7;
-    return lds_read_tr(blk + rb.v[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
-  };
 
   f32x4 pr[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) pr[j] = partner[j * 64 + lane];
-  bf16x8 abuf[DQ];
-  if constexpr (HAS_NEXT) {
-#pragma unroll
-    for (int u = 0; u < DQ; ++u) abuf[u] = qk_read(u);
-  }
+  KStream<Kv> kst{blk_next, &rb};
+  if constexpr (HAS_NEXT) kst.start();
   __builtin_amdgcn_sched_barrier(0);
 
   f32x16 x;
   f32x16 n0 = {};
   float m_use = 0.0f, psum = 0.0f;
   bf16x8 pa[2];
-  bf16x4 vb0[DV], vb1[DV];
+  VStream<Kv> vst{blk, &rb};
 
   // ---- S^T of block i + 1 on the MFMA pipe, the softmax step of block i in between
 #pragma unroll
   for (int kk = 0; kk < kQStepsPerWave; ++kk) {
     if constexpr (HAS_NEXT) {
-      n0 = mfma32(abuf[kk % DQ], qreg[kk], n0);
-      if (kk + DQ < kQStepsPerWave) abuf[kk % DQ] = qk_read(kk + DQ);
-      if (kk & 1) dma16(job.src, so.off[kk >> 1], job.dst + (kk >> 1) * 1024);
+      n0 = mfma32(kst.next(kk), qreg[kk], n0);
+      if ((kk & 1) && (kk >> 1) < Kv::kCopies)
+        dma16(job.src, so.off[kk >> 1], job.dst + (kk >> 1) * 1024);
     }
     if (kk == 0) {
       // full scores: own half + partner half (the same sum on both waves of the pair,
@@ -293,12 +507,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
           pbf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pa[ks][k], pa[ks][k + 1]}, ones, pbf, false);
       ws.l_bf += pbf;
     } else if (kk == 12) {
-      // the first V operands of block i
-#pragma unroll
-      for (int u = 0; u < DV; ++u) {
-        vb0[u] = pv_read(u, 0);
-        vb1[u] = pv_read(u, 1);
-      }
+      vst.start();  // the first V operands of block i
     }
     if (HAS_NEXT && kk == kQStepsPerWave - 1) __syncthreads();  // block i's halves are read
     __builtin_amdgcn_sched_barrier(0);
@@ -307,14 +516,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
   // ---- O += P V, V = this wave's 256 c_kv columns of block i, read transposed
 #pragma unroll
   for (int t = 0; t < NPV; ++t) {
-    const int u = t % DV;
-    const bf16x8 bv = {vb0[u][0], vb0[u][1], vb0[u][2], vb0[u][3],
-                       vb1[u][0], vb1[u][1], vb1[u][2], vb1[u][3]};
-    ws.acc[t & 7] = mfma32(pa[t >> 3], bv, ws.acc[t & 7]);
-    if (t + DV < NPV) {
-      vb0[u] = pv_read(t + DV, 0);
-      vb1[u] = pv_read(t + DV, 1);
-    }
+    ws.acc[t & 7] = mfma32(pa[t >> 3], vst.next(t), ws.acc[t & 7]);
     if constexpr (HAS_NEXT) {
       if (t == 8) {  // block i + 1's half is complete
         store_partial(own, n0);
@@ -334,7 +536,9 @@ __device__ __forceinline__ void write_rows(const SplitArgs& a, const WaveState& 
   const int lane = threadIdx.x & 63;
   const int M = a.M;
   const bool seen = l_tot > 0.0f;
-  const float inv = (seen && l_bf > 0.0f) ? 1.0f / l_bf : 0.0f;
+  // O = kv_scale * sum(P V) / sum(P): an E4M3 pool's scale enters here and in the
+  // score scale (1 for bf16)
+  const float inv = (seen && l_bf > 0.0f) ? a.kv_scale / l_bf : 0.0f;
   const float lse2 = seen ? ws.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
   float* base = whole ? a.O + ((size_t)b * M + m_slice) * kNope
                       : a.part_o + ((size_t)slot * a.slot_rows + row_in_tile) * kNope;
@@ -385,15 +589,17 @@ __device__ __forceinline__ void load_page_ids(const SplitArgs& a, PageIds& pi, i
 
 // Ring slot of block i.  The byte offset is passed through an empty asm so that the
 // compiler keeps it a scalar added to a few per-lane bases, instead of strength-
-// reducing i % kStages into one loop-carried register per LDS read.
+// reducing i % kStagesN into one loop-carried register per LDS read.
+template <class Kv>
 __device__ __forceinline__ uint8_t* ring_slot(uint8_t* ring, int i) {
-  uint32_t off = (uint32_t)(i % kStages) * kStageBytes;
+  uint32_t off = (uint32_t)(i % Kv::kStagesN) * Kv::kSlot;
   asm volatile("" : "+s"(off));
   return ring + off;
 }
 
 // Pool address of block i of the piece (logical page lo + i / 2, half i % 2) and the
 // number of its rows inside the request.
+template <class Kv>
 __device__ __forceinline__ const uint8_t* block_source(const SplitArgs& a, PageIds& pi, int b,
                                                        int lo, int hi, int L, int i,
                                                        int& valid) {
@@ -402,22 +608,32 @@ __device__ __forceinline__ const uint8_t* block_source(const SplitArgs& a, PageI
   const uint32_t phys = __builtin_amdgcn_readlane(pi.id, pg - pi.first);
   valid = min(kKvBlock, L - pg * kPage - half * kKvBlock);
   return reinterpret_cast<const uint8_t*>(a.kv_pool) +
-         ((size_t)phys * kPageBytes + (size_t)half * kStageBytes);
+         ((size_t)phys * Kv::kPageB + (size_t)half * Kv::kHalfB);
 }
 
-// Waits until at most one step's worth of this wave's copies (kStageCopiesPerWave)
-// is in flight; copies complete in issue order.
-__device__ __forceinline__ void wait_all_but_one_block() {
-  static_assert(kStageCopiesPerWave == 9, "vmcnt immediate below");
-  asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+// Waits until at most `sets` blocks' worth of this wave's copies are in flight
+// (copies complete in issue order; sets = 0..4).
+template <int kCopies>
+__device__ __forceinline__ void wait_copy_sets(int sets) {
+  static_assert(kCopies * 4 <= 63, "vmcnt immediate");
+  switch (sets) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies) : "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kCopies) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kCopies) : "memory"); break;
+  }
 }
 
 // One piece: logical pages [lo, hi) of request b against M-tile mt.  The pages are
-// walked as 32-row blocks through a ring of kStages half-page slots: while block i
-// is scored (softmax, P V) and block i + 1's S^T is computed, blocks i + 2 and i + 3
+// walked as 32-row blocks through a ring of kStagesN slots: while block i is scored
+// (softmax, P V) and block i + 1's S^T is computed, blocks i + 2 .. i + kStagesN - 1
 // are in flight.
+template <class Kv>
 __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32x4* xbuf, int b,
                                           int L, int mt, int lo, int hi, bool whole, int slot) {
+  constexpr int S = Kv::kStagesN;
+  constexpr int AHEAD = S - 1;  // blocks copied ahead of the one being scored
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = wave >> 1, c = wave & 1;  // row slice of the M-tile; contraction / column half
   const int M = a.M;
@@ -431,15 +647,15 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   const int n_vis_max = a.causal ? L - a.Sq + m_last / a.H + 1 : L;
   const int nb = max(0, min(2 * (hi - lo), (n_vis_max + kKvBlock - 1) / kKvBlock - 2 * lo));
 
-  // Q^T as the B operand of S^T = K Q^T: lane holds query row m_q,
-  // k = 16 (18 c + kk) + 8 (lane / 32) + 0..7
+  // Q^T as the B operand of S^T = K Q^T: lane holds query row m_q, for k-step kk the
+  // eight query elements from k = Kv::q_k(c, kk, lane / 32)
   bf16x8 qreg[kQStepsPerWave];
   {
-    const int kh = 8 * (lane >> 5);
+    const int h = lane >> 5;
     const size_t qrow = (size_t)b * M + (q_ok ? m_q : 0);
 #pragma unroll
     for (int kk = 0; kk < kQStepsPerWave; ++kk) {
-      const int k0 = (kQStepsPerWave * c + kk) * 16 + kh;
+      const int k0 = Kv::q_k(c, kk, h);
       bf16x8 v;
       if (k0 < kNope)
         v = *reinterpret_cast<const bf16x8*>(a.q_nope + qrow * kNope + k0);
@@ -451,8 +667,8 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
 
   WaveState ws;
   ws.m_seen = -INFINITY;
-  const ReadBases rb = read_bases(c);
-  const StageOffsets so = stage_offsets();
+  const typename Kv::Bases rb = Kv::bases(c);
+  const typename Kv::Offsets so = Kv::offsets();
   PageIds pi;
   load_page_ids(a, pi, b, lo, hi);
   wait_vmem_all();  // queries and page ids are in before any block copy is counted
@@ -460,6 +676,10 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   f32x4* own = xbuf + wave * 4 * 64;  // this wave's S^T half (4 x 64 lanes x f32x4)
   const f32x4* partner = xbuf + (wave ^ 1) * 4 * 64;
   auto lim_of = [&](int i) { return n_vis - (lo + (i >> 1)) * kPage - (i & 1) * kKvBlock; };
+  // copy sets issued after block i + 1's when iteration i starts: the prologue's
+  // later blocks plus one set per step (a tail block copied at an iteration's top
+  // only adds to that count)
+  const int sets_after = min(nb, AHEAD) - 2;
 
   // At most two passes: the second (rare) one starts from the rows' true maxima.
   for (int pass = 0; pass < 2; ++pass) {
@@ -468,67 +688,56 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     ws.m_ref = pass == 0 ? -INFINITY : ws.m_seen;
     ws.l_run = 0.0f;
     ws.l_bf = 0.0f;
-    // Block j is copied into ring slot j % 4 during iteration j - 3 (the slot's
-    // previous block, j - 4, was finished in iteration j - 4), its S^T halves are
+    // Block j is copied into ring slot j % S during iteration j - AHEAD (the slot's
+    // previous block, j - S, was finished in iteration j - S), its S^T halves are
     // computed in iteration j - 1 and its softmax and P V run in iteration j.  A
-    // request's partial last block is copied at the top of iteration j - 3 instead.
-    // Prologue: blocks 0..2 in flight, S^T halves of block 0.
+    // request's partial last block is copied at the top of iteration j - AHEAD
+    // instead.  Prologue: blocks 0 .. AHEAD - 1 in flight, S^T halves of block 0.
     wait_vmem_all();  // no copy of an earlier pass is still landing in the ring
-    const uint8_t* src_cur = nullptr;  // pool address of block i
-    const uint8_t* src_next = nullptr;  // ... of block i + 1
-    const uint8_t* src_ahead = nullptr;  // ... of block i + 2
-#pragma unroll 1
-    for (int j = 0; j < 3 && j < nb; ++j) {
-      int valid;
-      const uint8_t* src = block_source(a, pi, b, lo, hi, L, j, valid);
-      stage_block(src, ring_slot(ring, j), valid, so);
-      if (j == 0) src_cur = src;
-      if (j == 1) src_next = src;
-      if (j == 2) src_ahead = src;
+    const uint8_t* srcs[AHEAD];  // pool addresses of blocks i .. i + AHEAD - 1
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j) srcs[j] = nullptr;
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j) {
+      if (j < nb) {
+        int valid;
+        srcs[j] = block_source<Kv>(a, pi, b, lo, hi, L, j, valid);
+        Kv::stage(srcs[j], ring_slot<Kv>(ring, j), valid, so);
+      }
     }
-    if (nb >= 3)
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if (nb == 2)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      wait_vmem_all();
-    __syncthreads();  // block 0 is in LDS
+    wait_copy_sets<Kv::kCopies>(min(nb, AHEAD) - 1);  // block 0 has landed
+    __syncthreads();
     f32x16 s_own = {};  // this wave's half of S^T of the block being scored
     if (nb > 0) {
-      s_own = qk_partial(ring_slot(ring, 0), rb, qreg);
+      s_own = qk_partial<Kv>(ring_slot<Kv>(ring, 0), rb, qreg);
       store_partial(own, s_own);
     }
     int i = 0;
     for (; i + 1 < nb; ++i) {
-      // block i + 1 has landed ...  (at least one step's copies were issued after
-      // it, except when the piece has only two blocks)
-      if (i == 0 && nb < 3)
-        wait_vmem_all();
-      else
-        wait_all_but_one_block();
+      wait_copy_sets<Kv::kCopies>(sets_after);  // block i + 1 has landed ...
       // ... in every wave; both S^T halves of block i are in LDS; every wave is done
-      // with block i - 1, whose slot now receives block i + 3
+      // with block i - 1, whose slot now receives block i + AHEAD
       __syncthreads();
-      CopyJob job = copy_job(src_cur, ring_slot(ring, i));  // same-data re-copy
+      CopyJob job = copy_job<Kv>(srcs[0], ring_slot<Kv>(ring, i));  // same-data re-copy
       const uint8_t* src_new = nullptr;
-      if (i + 3 < nb) {
+      if (i + AHEAD < nb) {
         int valid;
-        src_new = block_source(a, pi, b, lo, hi, L, i + 3, valid);
+        src_new = block_source<Kv>(a, pi, b, lo, hi, L, i + AHEAD, valid);
         if (valid == kKvBlock)
-          job = copy_job(src_new, ring_slot(ring, i + 3));
+          job = copy_job<Kv>(src_new, ring_slot<Kv>(ring, i + AHEAD));
         else
-          stage_block(src_new, ring_slot(ring, i + 3), valid, so);
+          Kv::stage(src_new, ring_slot<Kv>(ring, i + AHEAD), valid, so);
       }
-      pipe_step<true>(ring_slot(ring, i), ring_slot(ring, i + 1), rb, qreg, s_own, own, partner,
-                      ws, lim_of(i), a.scale_log2, job, so);
-      src_cur = src_next;
-      src_next = src_ahead;
-      src_ahead = src_new;
+      pipe_step<true, Kv>(ring_slot<Kv>(ring, i), ring_slot<Kv>(ring, i + 1), rb, qreg, s_own,
+                          own, partner, ws, lim_of(i), a.scale_log2, job, so);
+#pragma unroll
+      for (int j = 0; j + 1 < AHEAD; ++j) srcs[j] = srcs[j + 1];
+      srcs[AHEAD - 1] = src_new;
     }
     if (i < nb) {  // the last block (already in LDS): nothing left to score ahead or copy
       __syncthreads();
-      pipe_step<false>(ring_slot(ring, i), nullptr, rb, qreg, s_own, own, partner, ws,
-                       lim_of(i), a.scale_log2, CopyJob{}, so);
+      pipe_step<false, Kv>(ring_slot<Kv>(ring, i), nullptr, rb, qreg, s_own, own, partner, ws,
+                           lim_of(i), a.scale_log2, CopyJob{}, so);
     }
     // a row whose scores outgrew its reference by more than the lazy bound forces a
     // second pass for the whole workgroup; the flag lives in the exchange buffer
@@ -548,10 +757,12 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
              whole, slot);
 }
 
+template <class Kv>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 splitkv_kernel(SplitArgs a) {
-  // 4 x 36 KB ring + 16 KB exchange buffer = the whole 160 KB of LDS
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
+  // bf16: 4 x 36 KB ring + 16 KB exchange buffer = the whole 160 KB of LDS;
+  // E4M3: 6 x 20 KB ring + 16 KB
+  __shared__ __attribute__((aligned(16))) uint8_t ring[Kv::kStagesN * Kv::kSlot];
   __shared__ f32x4 xbuf[kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
   static_assert(sizeof(f32x4) * kWaves * 4 * 64 >= (2 * kMaxBatch + 1) * sizeof(int),
                 "the page prefix and lengths are built in the exchange buffer");
@@ -588,10 +799,10 @@ splitkv_kernel(SplitArgs a) {
       const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
       const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
       const bool whole = plo == 0 && phi == pb1 - pb0;
-      run_piece(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
-                __builtin_amdgcn_readfirstlane(Lb), mt,
-                __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi), whole,
-                (b + g) * a.n_mt + mt);
+      run_piece<Kv>(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
+                    __builtin_amdgcn_readfirstlane(Lb), mt,
+                    __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi),
+                    whole, (b + g) * a.n_mt + mt);
       __syncthreads();  // LDS free before the next piece stages into it
     }
     pb0 = pb1;
@@ -822,7 +1033,10 @@ __global__ void __launch_bounds__(kCombineThreads) combine_rows_kernel(CombineAr
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.G * a.n_mt;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(splitkv_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+  if (a.kv_e4m3)
+    hipLaunchKernelGGL(splitkv_kernel<E4m3Kv>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(splitkv_kernel<Bf16Kv>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -112,15 +112,21 @@ _E4M3_POS = _e4m3_positive_values()
 
 def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     """Round finite float32 values to OCP FP8 E4M3 codes: nearest value, ties to the
-    even code, magnitudes beyond 448 saturated to 448.  Returns uint8 codes."""
+    even code, magnitudes beyond 448 saturated to 448.  Returns uint8 codes.
+
+    Normal results (|x| >= 2^-6) keep 3 mantissa bits: the float32 pattern is rounded
+    to nearest-even at bit 20 and re-biased from exponent 127 to 7.  Below 2^-6 the
+    codes are the multiples of 2^-9 (subnormals; 8 * 2^-9 is the smallest normal,
+    whose code is also 8), so the code is rint(|x| * 512)."""
     x = np.asarray(x, dtype=np.float32)
-    a = np.minimum(np.abs(x).astype(np.float64), E4M3_MAX)
-    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
-    lo = np.maximum(hi - 1, 0)
-    d_lo = a - _E4M3_POS[lo]
-    d_hi = _E4M3_POS[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    a = np.minimum(np.abs(x), np.float32(E4M3_MAX))
+    bits = a.view(np.uint32)
+    r = (bits + np.uint32(0x7FFFF) + ((bits >> np.uint32(20)) & np.uint32(1))) \
+        & np.uint32(0xFFF00000)
+    exp = ((r >> np.uint32(23)).astype(np.int32) - 127 + 7).clip(0, 15)
+    normal = ((exp << 3) | ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32))
+    sub = np.rint(a * np.float32(512.0)).astype(np.int32)
+    code = np.where(a < np.float32(2.0 ** -6), sub, normal).astype(np.uint8)
     return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
 
 

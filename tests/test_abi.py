@@ -21,8 +21,8 @@ FAKE = 0x10000  # 16-byte aligned host address; never dereferenced by the host c
 def test_library_exports_every_header_function():
     names = mla.header_functions()
     assert names == sorted([
-        "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_splitkv",
-        "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
+        "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
+        "mla_decode_splitkv", "mla_decode_splitkv_e4m3", "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
         "mla_status_string"])
     L = mla.lib()
     for n in names:
@@ -78,16 +78,23 @@ def test_workspace_size_rejects(args, code):
 def _call(name="mla_decode", **over):
     a = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, num_pages=8, page_size=64,
              block_table=FAKE, max_pages=4, seq_lens=FAKE, B=1, Sq=1, H=16, scale=0.07,
-             causal=1, parts=2, O=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+             causal=1, parts=2, O=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None,
+             kv_scale=0.015625)
     a.update(over)
     fn = getattr(mla.lib(), name)
-    return fn(a["q_nope"], a["q_rope"], a["kv_pool"], a["num_pages"], a["page_size"],
+    # the E4M3 entry points take the pool's scale right after the pool
+    pool = ((a["kv_pool"], a["kv_scale"]) if name.endswith("_e4m3") else (a["kv_pool"],))
+    return fn(a["q_nope"], a["q_rope"], *pool, a["num_pages"], a["page_size"],
               a["block_table"], a["max_pages"], a["seq_lens"], a["B"], a["Sq"], a["H"],
               a["scale"], a["causal"], a["parts"], a["O"], a["lse"], a["ws"], a["ws_bytes"],
               a["stream"])
 
 
-@pytest.mark.parametrize("name", ["mla_decode", "mla_decode_splitkv", "mla_prefill_with_prefix"])
+COMPUTE_ENTRY_POINTS = ["mla_decode", "mla_decode_splitkv", "mla_prefill_with_prefix",
+                        "mla_decode_e4m3", "mla_decode_splitkv_e4m3"]
+
+
+@pytest.mark.parametrize("name", COMPUTE_ENTRY_POINTS)
 @pytest.mark.parametrize("over,code", [
     (dict(q_nope=None), INVALID), (dict(q_rope=None), INVALID), (dict(kv_pool=None), INVALID),
     (dict(block_table=None), INVALID), (dict(seq_lens=None), INVALID), (dict(O=None), INVALID),
@@ -102,6 +109,12 @@ def _call(name="mla_decode", **over):
 ])
 def test_compute_entry_points_reject_on_host(name, over, code):
     assert _call(name, **over) == code
+
+
+@pytest.mark.parametrize("name", ["mla_decode_e4m3", "mla_decode_splitkv_e4m3"])
+@pytest.mark.parametrize("kv_scale", [0.0, -1.0, math.nan, math.inf, -math.inf])
+def test_e4m3_entry_points_reject_bad_scale(name, kv_scale):
+    assert _call(name, kv_scale=kv_scale) == INVALID
 
 
 def test_workspace_one_byte_short_is_rejected():
