@@ -220,6 +220,18 @@ def main():
     torch.cuda.synchronize()
     split_b2b = kev[0].elapsed_time(kev[1]) / args.steps
 
+    # The same steps in one launch each (mla_decode_single_pass), for comparison.
+    single_pass_us = None
+    if G > 1:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            calls[i % n_copies].single_pass()
+        torch.cuda.synchronize()
+        single_pass_us = (time.perf_counter() - t0) * 1e6 / args.steps
+        if mla.read_error_flags(ws):
+            raise SystemExit("kernel reported a data fault flag")
+
     if args.copy_probe:
         from mla_latent_kv_16_amd.profiling import COPY_PROBE_BYTES
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -284,6 +296,7 @@ def main():
         "split_pass_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
                                   round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
         "split_kernel_us_back_to_back": round(split_b2b * 1e3, 2),
+        "single_pass_us_per_step": None if single_pass_us is None else round(single_pass_us, 2),
         "split_pass_hbm_frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
         "split_pass_mfma_frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof,

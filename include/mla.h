@@ -66,6 +66,9 @@ typedef enum {
 /* Device-side data faults reported through the workspace header. */
 #define MLA_FLAG_BAD_SEQ_LEN 1u  /* some seq_lens[b] < Sq or > 64 * max_pages_per_seq */
 #define MLA_FLAG_BAD_PAGE_ID 2u  /* some visible block_table entry outside [0, num_pages) */
+#define MLA_FLAG_MERGE_WAIT 4u   /* a single-pass merge gave up waiting (one second) for the
+                                    partials of its request: its outputs are unspecified and
+                                    the workspace must be zero-filled again before reuse */
 
 #define MLA_PAGE_SIZE 64
 #define MLA_NOPE_DIM 512
@@ -86,8 +89,9 @@ int mla_decode_auto_partitions(int B, int Sq, int H, int max_pages_per_seq,
                                int* num_partitions);
 
 /*
- * Workspace bytes a decode or prefill call with these sizes needs (partial
- * results of the split-KV pass plus a 256-byte header holding the error flags).
+ * Workspace bytes a decode or prefill call with these sizes needs (a 256-byte
+ * header holding the error flags, then, when the call splits the KV, the
+ * single-pass arrival counters and the partial results of the split-KV pass).
  * num_partitions = 0 means the automatic count on the current device.
  */
 int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq,
@@ -96,10 +100,10 @@ int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq,
 /*
  * Speculative-verify / plain decode over the paged latent cache ("Faster kernels,
  * slower engine", §7.1 Gluon MLA decode: a split-KV pass that materialises
- * partial results and a second pass that reduces them; the query-length axis is
- * folded into the head axis to fill the matrix tile: TokenSpeed launch news,
- * decode-kernel paragraph).  Enqueues the split-KV pass and, when
- * num_partitions > 1, the log-sum-exp combine pass.
+ * partial results and a second pass that reduces them by their log-sum-exp; the
+ * query-length axis is folded into the head axis to fill the matrix tile:
+ * TokenSpeed launch news, decode-kernel paragraph).  Enqueues the split-KV pass
+ * and, when num_partitions > 1, the merge pass.
  *
  *   q_nope       bf16 [B, Sq, H, 512]   query with the key up-projection absorbed
  *   q_rope       bf16 [B, Sq, H, 64]    rotated RoPE part of the query
@@ -113,8 +117,10 @@ int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq,
  *   O            fp32 [B, Sq, H, 512]   output (written)
  *   lse          fp32 [B, Sq, H]        natural-log log-sum-exp of the scaled scores
  *   workspace    device buffer of at least mla_decode_workspace_size() bytes,
- *                16-byte aligned.  Its first 256 bytes (the error-flag header) must
- *                be zero before its first use; the rest needs no initialisation.
+ *                16-byte aligned, zero-filled before its first use (the error-flag
+ *                header and the single-pass counters must start at zero; every
+ *                call leaves the counters at zero again, so a workspace is zeroed
+ *                once).
  */
 int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
                int64_t num_pages, int page_size,
@@ -123,12 +129,29 @@ int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* k
                float* O, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same decode in ONE launch ("Faster kernels, slower engine", §7.1: a
+ * hand-written kernel can skip the second pass).  Workgroups appended to the
+ * split-KV grid merge each request's partials as soon as its pieces have published
+ * them through counters in the workspace.  Same arguments, meaning and results (bit
+ * for bit) as mla_decode.  On MI355X it is slower than the two launches: publishing
+ * the partials across the eight XCDs' L2 caches costs more than the second launch
+ * saves.  Calls that share a workspace must not overlap.
+ */
+int mla_decode_single_pass(const uint16_t* q_nope, const uint16_t* q_rope,
+                           const uint16_t* kv_pool, int64_t num_pages, int page_size,
+                           const int32_t* block_table, int max_pages_per_seq,
+                           const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                           int causal, int num_partitions, float* O, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * The two passes of mla_decode as separate calls, for callers that schedule or
- * time them apart.  Same arguments and meaning; both calls of one decode must use
- * the same sizes, num_partitions and workspace.  mla_decode_splitkv writes the
- * final O/lse of every request that one partition covers whole and partial results
- * for the others; mla_decode_combine merges those partials (and is a no-op when
- * the partition count is 1).
+ * time them apart.  Same arguments and meaning, and the same results as mla_decode
+ * bit for bit; both calls of one decode must use the same sizes, num_partitions
+ * and workspace.
+ * mla_decode_splitkv writes the final O/lse of every request that one partition
+ * covers whole and partial results for the others; mla_decode_combine merges those
+ * partials (and is a no-op when the partition count is 1).
  */
 int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
                        int64_t num_pages, int page_size,
@@ -166,7 +189,8 @@ int mla_prefill_with_prefix(const uint16_t* q_nope, const uint16_t* q_rope,
  *             must be finite and > 0 (else MLA_ERR_INVALID_ARG)
  *
  * Every other argument, the workspace and the outputs are as for mla_decode /
- * mla_decode_splitkv; the combine pass is mla_decode_combine.  The scores and P V
+ * mla_decode_splitkv / mla_decode_single_pass; the combine pass is
+ * mla_decode_combine.  The scores and P V
  * run in bf16 on the exact widening of the codes (every E4M3 value is a bf16 value),
  * with kv_scale folded into the softmax scale and into O.
  */
@@ -181,6 +205,13 @@ int mla_decode_splitkv_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
                             const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
                             int causal, int num_partitions, float* O, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
+int mla_decode_single_pass_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
+                                const uint8_t* kv_pool, float kv_scale, int64_t num_pages,
+                                int page_size, const int32_t* block_table, int max_pages_per_seq,
+                                const int32_t* seq_lens, int B, int Sq, int H,
+                                float softmax_scale, int causal, int num_partitions, float* O,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * Waits for `stream`, then copies the workspace header's error flags

@@ -13,6 +13,8 @@ from ._binding import (  # noqa: F401
     decode,
     decode_combine,
     decode_e4m3,
+    decode_single_pass,
+    decode_single_pass_e4m3,
     decode_splitkv,
     decode_splitkv_e4m3,
     header_functions,

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "mla_decode_splitkv": (_COMPUTE_ARGS, _i32),
     "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
     "mla_decode_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
+    "mla_decode_single_pass": (_COMPUTE_ARGS, _i32),
+    "mla_decode_single_pass_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_splitkv_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_combine": ([_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_read_error_flags": ([_vp, _vp, ctypes.POINTER(ctypes.c_uint32)], _i32),
@@ -218,11 +220,29 @@ def decode_splitkv_e4m3(q_nope, q_rope, kv_pool, kv_scale, block_table, seq_lens
                          workspace, stream)
 
 
+def decode_single_pass_e4m3(q_nope, q_rope, kv_pool, kv_scale, block_table, seq_lens,
+                            softmax_scale, causal=True, num_partitions=0, out=None, lse=None,
+                            workspace=None, stream=None):
+    """mla_decode_single_pass_e4m3: the E4M3-pool decode in one launch."""
+    return _compute_e4m3("mla_decode_single_pass_e4m3", q_nope, q_rope, kv_pool, kv_scale,
+                         block_table, seq_lens, softmax_scale, causal, num_partitions, out, lse,
+                         workspace, stream)
+
+
 def decode(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
            num_partitions=0, out=None, lse=None, workspace=None, stream=None):
     """mla_decode: split-KV pass + combine pass.  Returns (O fp32 [B,Sq,H,512], lse fp32 [B,Sq,H])."""
     return _compute("mla_decode", q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale,
                     causal, num_partitions, out, lse, workspace, stream)
+
+
+def decode_single_pass(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale,
+                       causal=True, num_partitions=0, out=None, lse=None, workspace=None,
+                       stream=None):
+    """mla_decode_single_pass: the same decode in one launch (merging workgroups appended
+    to the split-KV grid)."""
+    return _compute("mla_decode_single_pass", q_nope, q_rope, kv_pool, block_table, seq_lens,
+                    softmax_scale, causal, num_partitions, out, lse, workspace, stream)
 
 
 def decode_splitkv(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
@@ -287,12 +307,17 @@ class BoundDecode:
         L = lib()
         if e4m3:
             self._decode, self._split = L.mla_decode_e4m3, L.mla_decode_splitkv_e4m3
+            self._single = L.mla_decode_single_pass_e4m3
         else:
             self._decode, self._split = L.mla_decode, L.mla_decode_splitkv
+            self._single = L.mla_decode_single_pass
         self._combine = L.mla_decode_combine
 
     def __call__(self):
         _check(self._decode(*self._args), "mla_decode")
+
+    def single_pass(self):
+        _check(self._single(*self._args), "mla_decode_single_pass")
 
     def splitkv(self):
         _check(self._split(*self._args), "mla_decode_splitkv")

@@ -74,9 +74,15 @@ int resolve_partitions(const Geometry& g, int B, int max_pages, int requested, i
   return MLA_OK;
 }
 
+// Single-pass counters: arrive[B * n_mt] and done[B * n_mt], after the header.
+size_t counter_bytes(const Geometry& g, int B) {
+  return ((size_t)2 * B * g.n_mt * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
 size_t workspace_bytes_for(const Geometry& g, int B, int G) {
   size_t bytes = kHeaderBytes;
   if (G > 1) {
+    bytes += counter_bytes(g, B);
     const size_t slots = (size_t)(B + G) * g.n_mt;
     bytes += slots * g.slot_rows * kNope * sizeof(float);   // partial O
     bytes += ((slots * g.slot_rows * sizeof(float)) + 255) & ~(size_t)255;  // partial LSE
@@ -86,17 +92,23 @@ size_t workspace_bytes_for(const Geometry& g, int B, int G) {
 
 struct Layout {
   uint32_t* flags;
+  uint32_t* arrive;
+  uint32_t* done;
   float* part_o;
   float* part_lse;
 };
 
+// [256-byte header | counters | partial O | partial LSE]; only the header when G = 1
 Layout carve(void* ws, const Geometry& g, int B, int G) {
   Layout l;
   uint8_t* base = static_cast<uint8_t*>(ws);
   l.flags = reinterpret_cast<uint32_t*>(base);
   const size_t slots = (size_t)(B + G) * g.n_mt;
-  l.part_o = reinterpret_cast<float*>(base + kHeaderBytes);
-  l.part_lse = reinterpret_cast<float*>(base + kHeaderBytes + slots * g.slot_rows * kNope * 4);
+  const size_t cnt = G > 1 ? counter_bytes(g, B) : 0;
+  l.arrive = reinterpret_cast<uint32_t*>(base + kHeaderBytes);
+  l.done = l.arrive + (size_t)B * g.n_mt;
+  l.part_o = reinterpret_cast<float*>(base + kHeaderBytes + cnt);
+  l.part_lse = reinterpret_cast<float*>(base + kHeaderBytes + cnt + slots * g.slot_rows * kNope * 4);
   return l;
 }
 
@@ -140,7 +152,7 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
                   const void* kv_pool, int kv_e4m3, float kv_scale, int64_t num_pages,
                   const int32_t* block_table, int max_pages, const int32_t* seq_lens, int B,
                   int Sq, int H, float scale, int causal, float* O, float* lse,
-                  hipStream_t stream) {
+                  bool single_pass, hipStream_t stream) {
   SplitArgs a;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
@@ -165,6 +177,23 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
   a.kv_e4m3 = kv_e4m3;
   a.kv_scale = kv_scale;
   a.scale_log2 = scale * kv_scale * 1.4426950408889634f;
+  a.n_split = c.G * c.geo.n_mt;
+  a.arrive = nullptr;
+  a.done = nullptr;
+  a.comb_rows = 0;
+  if (single_pass && c.G > 1) {
+    a.arrive = c.lay.arrive;
+    a.done = c.lay.done;
+    // as for the separate combine: a workgroup per row when there are many pieces
+    // per request, else waves over runs of rows, about one workgroup per CU
+    if ((int64_t)c.G < 16 * (int64_t)B) {
+      int cus = 0;
+      if (cu_count(&cus) != MLA_OK) return MLA_ERR_HIP;
+      const int64_t rows = (int64_t)B * c.geo.M;
+      const int64_t per_wave = (rows + (int64_t)kWaves * cus - 1) / ((int64_t)kWaves * cus);
+      a.comb_rows = (int)(per_wave < 1 ? 1 : per_wave);
+    }
+  }
   return launch_splitkv(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -178,6 +207,8 @@ int enqueue_combine(const Call& c, const int32_t* seq_lens, int max_pages, int B
   a.part_o = c.lay.part_o;
   a.part_lse = c.lay.part_lse;
   a.flags = c.lay.flags;
+  a.arrive = nullptr;
+  a.done = nullptr;
   a.max_pages = max_pages;
   a.B = B;
   a.Sq = Sq;
@@ -188,6 +219,27 @@ int enqueue_combine(const Call& c, const int32_t* seq_lens, int max_pages, int B
   a.MT = c.geo.mt_rows;
   a.slot_rows = c.geo.slot_rows;
   return launch_combine(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// One decode: the split-KV pass, then the separate merge kernel, or both in one
+// launch (single_pass).
+int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool, int kv_e4m3,
+                float kv_scale, int64_t num_pages, int page_size, const int32_t* block_table,
+                int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
+                float softmax_scale, int causal, int num_partitions, float* O, float* lse,
+                void* workspace, size_t workspace_bytes, void* stream, bool single_pass) {
+  if (kv_e4m3 && (!(kv_scale > 0.0f) || isinf(kv_scale))) return MLA_ERR_INVALID_ARG;
+  Call c;
+  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                   workspace_bytes, &c);
+  if (st != MLA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = enqueue_split(c, q_nope, q_rope, kv_pool, kv_e4m3, kv_scale, num_pages, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
+                     single_pass, s);
+  if (st != MLA_OK || single_pass) return st;
+  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
 }
 
 }  // namespace
@@ -238,7 +290,7 @@ int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uin
   if (st != MLA_OK) return st;
   return enqueue_split(c, q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, block_table,
                        max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
-                       static_cast<hipStream_t>(stream));
+                       false, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_combine(const int32_t* seq_lens, int max_pages_per_seq, int B, int Sq, int H,
@@ -263,16 +315,20 @@ int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* k
                int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
                float softmax_scale, int causal, int num_partitions, float* O, float* lse,
                void* workspace, size_t workspace_bytes, void* stream) {
-  Call c;
-  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
-                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
-                   workspace_bytes, &c);
-  if (st != MLA_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = enqueue_split(c, q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, block_table,
-                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse, s);
-  if (st != MLA_OK) return st;
-  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
+  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
+                     num_partitions, O, lse, workspace, workspace_bytes, stream, false);
+}
+
+int mla_decode_single_pass(const uint16_t* q_nope, const uint16_t* q_rope,
+                           const uint16_t* kv_pool, int64_t num_pages, int page_size,
+                           const int32_t* block_table, int max_pages_per_seq,
+                           const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                           int causal, int num_partitions, float* O, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
+                     num_partitions, O, lse, workspace, workspace_bytes, stream, true);
 }
 
 int mla_prefill_with_prefix(const uint16_t* q_nope, const uint16_t* q_rope,
@@ -300,7 +356,7 @@ int mla_decode_splitkv_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
   if (st != MLA_OK) return st;
   return enqueue_split(c, q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, block_table,
                        max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
-                       static_cast<hipStream_t>(stream));
+                       false, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* kv_pool,
@@ -308,17 +364,21 @@ int mla_decode_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_
                     int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
                     float softmax_scale, int causal, int num_partitions, float* O, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (!(kv_scale > 0.0f) || isinf(kv_scale)) return MLA_ERR_INVALID_ARG;
-  Call c;
-  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
-                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
-                   workspace_bytes, &c);
-  if (st != MLA_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = enqueue_split(c, q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, block_table,
-                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse, s);
-  if (st != MLA_OK) return st;
-  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
+  return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
+                     num_partitions, O, lse, workspace, workspace_bytes, stream, false);
+}
+
+int mla_decode_single_pass_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
+                                const uint8_t* kv_pool, float kv_scale, int64_t num_pages,
+                                int page_size, const int32_t* block_table, int max_pages_per_seq,
+                                const int32_t* seq_lens, int B, int Sq, int H,
+                                float softmax_scale, int causal, int num_partitions, float* O,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
+                     num_partitions, O, lse, workspace, workspace_bytes, stream, true);
 }
 
 int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {

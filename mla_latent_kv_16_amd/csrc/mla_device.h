@@ -19,6 +19,7 @@ constexpr int kPageBytes = kPage * kRowBytes;  // 73,728
 constexpr int kMaxBatch = 1024;
 constexpr uint32_t kFlagBadSeqLen = 1u;
 constexpr uint32_t kFlagBadPageId = 2u;
+constexpr uint32_t kFlagMergeWait = 4u;  // a merge gave up waiting for its pieces
 constexpr int kHeaderBytes = 256;
 
 // Split-KV pass: a workgroup is 4 waves and covers an M-tile of 64 folded query

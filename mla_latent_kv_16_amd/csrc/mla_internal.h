@@ -28,6 +28,14 @@ struct SplitArgs {
   int kv_e4m3;                 // 1: the pool holds E4M3 codes scaled by kv_scale
   float kv_scale;              // dequantization scale of the pool (1 for bf16)
   float scale_log2;            // softmax_scale * kv_scale * log2(e)
+  // Single pass (arrive != nullptr): workgroups past the first n_split merge the
+  // partials.  A piece bumps arrive[b * n_mt + mt] once its partial is written; a
+  // merged row bumps done[b * n_mt + mt], and the last row of the M-tile returns
+  // both counters to zero.
+  uint32_t* arrive;            // [B * n_mt]
+  uint32_t* done;              // [B * n_mt]
+  int n_split;                 // split-KV workgroups (G * n_mt)
+  int comb_rows;               // single pass: 0 = a workgroup per row, else rows per wave
 };
 
 struct CombineArgs {
@@ -37,6 +45,8 @@ struct CombineArgs {
   const float* part_o;
   const float* part_lse;
   uint32_t* flags;
+  uint32_t* arrive;            // single pass: wait for the pieces (nullptr: two passes)
+  uint32_t* done;
   int max_pages;
   int B, Sq, H, M;
   int n_mt, G, MT, slot_rows;

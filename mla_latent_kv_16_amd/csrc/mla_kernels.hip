@@ -757,59 +757,50 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
              whole, slot);
 }
 
-template <class Kv>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-splitkv_kernel(SplitArgs a) {
-  // bf16: 4 x 36 KB ring + 16 KB exchange buffer = the whole 160 KB of LDS;
-  // E4M3: 6 x 20 KB ring + 16 KB
-  __shared__ __attribute__((aligned(16))) uint8_t ring[Kv::kStagesN * Kv::kSlot];
-  __shared__ f32x4 xbuf[kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
-  static_assert(sizeof(f32x4) * kWaves * 4 * 64 >= (2 * kMaxBatch + 1) * sizeof(int),
-                "the page prefix and lengths are built in the exchange buffer");
+// ---- combine ---------------------------------------------------------------------
+// The partials of a split request are merged by their log-sum-exp.  The same row
+// merges serve the separate combine kernels (after the split-KV kernel) and the
+// single-pass kernel, whose workgroups past the split-KV ones wait for the pieces of
+// their request first.
 
-  const int lam = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int g = lam / a.n_mt;
-  const int mt = lam - g * a.n_mt;
+// Single pass: a merge waits until `expected` pieces of its (request, M-tile) have
+// published their partials.  The split-KV workgroups never wait and, launched ahead
+// of every merging workgroup of the grid, are all dispatched before any merging one;
+// so every awaited piece runs.  The wait is still bounded (kMergeWaitTicks of the
+// constant 100 MHz clock): past it the merge raises kFlagMergeWait and proceeds.
+constexpr uint64_t kMergeWaitTicks = 100000000ull;  // one second
 
-  // page prefix and clamped lengths of the batch, in the exchange buffer until the
-  // first piece starts
-  int* prefix = reinterpret_cast<int*>(xbuf);
-  int* lens = prefix + kMaxBatch + 1;
-  build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, true, lens);
-  const int64_t T = prefix[a.B];
-  const int64_t p0 = part_begin(T, a.G, g);
-  const int64_t p1 = part_begin(T, a.G, g + 1);
-  // first request whose pages reach past p0
-  int lo = 0, hi = a.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid + 1] > p0) hi = mid; else lo = mid + 1;
-  }
-  int pb0 = prefix[lo];
-  const int L_first = lens[lo];
-  __syncthreads();  // the prefix has been read
-  if (p0 >= p1) return;
-
-  // walk the requests the partition touches; a request's page count is recomputed
-  // from its clamped length (the same count the prefix was built from)
-  for (int b = lo; b < a.B && pb0 < p1; ++b) {
-    const int Lb = b == lo ? L_first : clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
-    const int pb1 = pb0 + (Lb + kPage - 1) / kPage;
-    if (pb1 > pb0) {
-      const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
-      const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
-      const bool whole = plo == 0 && phi == pb1 - pb0;
-      run_piece<Kv>(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
-                    __builtin_amdgcn_readfirstlane(Lb), mt,
-                    __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi),
-                    whole, (b + g) * a.n_mt + mt);
-      __syncthreads();  // LDS free before the next piece stages into it
+__device__ __forceinline__ void wait_pieces(const uint32_t* ctr, uint32_t expected,
+                                            uint32_t* flags) {
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expected) {
+    __builtin_amdgcn_s_sleep(4);
+    if (wall_clock64() - t0 > kMergeWaitTicks) {
+      atomicOr(flags, kFlagMergeWait);
+      break;
     }
-    pb0 = pb1;
   }
 }
 
-// ---- combine ---------------------------------------------------------------------
+// Non-empty partitions among g0..g1: the pieces of a request that spans them.
+__device__ __forceinline__ uint32_t pieces_of(int64_t T, int G, int g0, int g1, bool dense) {
+  if (dense) return (uint32_t)(g1 - g0 + 1);
+  uint32_t n = 0;
+  for (int g = g0; g <= g1; ++g) n += part_begin(T, G, g) < part_begin(T, G, g + 1) ? 1u : 0u;
+  return n;
+}
+
+// Single pass: one more row of M-tile (b, mt) is merged; the last of its rows
+// returns both counters to zero for the next call (every merge of the tile has
+// finished waiting by then).
+__device__ __forceinline__ void row_merged(const CombineArgs& a, int idx, int mt) {
+  const uint32_t rows = (uint32_t)min(a.M - mt * a.MT, a.MT);
+  if (atomicAdd(a.done + idx, 1u) + 1u == rows) {
+    atomicExch(a.arrive + idx, 0u);
+    atomicExch(a.done + idx, 0u);
+  }
+}
+
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
@@ -836,22 +827,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
-// Combine, many pieces per request (G >= 16 B): one workgroup per folded query row
-// (b, m) of a split request.  Thread t handles columns 8 (t % 64) .. + 8 of the
-// pieces s with s % 4 == t / 64.  The partial outputs of a chunk of 64 pieces (16
-// per thread) are all requested at once, before the row's log-sum-exp over the
-// pieces is reduced, so that one memory round trip covers both; the four piece
-// lanes are summed through LDS.
+// Many pieces per request (G >= 16 B): one workgroup merges folded query row `row`
+// = (b, m).  Thread t handles columns 8 (t % 64) .. + 8 of the pieces s with
+// s % 4 == t / 64.  The partial outputs of a chunk of 64 pieces (16 per thread) are
+// all requested at once, before the row's log-sum-exp over the pieces is reduced,
+// so that one memory round trip covers both; the four piece lanes are summed
+// through LDS.  prefix: kMaxBatch + 1 ints, red: 4 floats, part: 4 x 512 floats.
 constexpr int kCombineLanes = kCombineThreads / 64;
 constexpr int kCombineChunk = 16;  // pieces per thread per chunk
 
-__global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
-  __shared__ int prefix[kMaxBatch + 1];
-  __shared__ float red[kCombineLanes];
-  __shared__ __attribute__((aligned(16))) float part[kCombineLanes][64 * 8];
+__device__ __forceinline__ void merge_row_group(const CombineArgs& a, int row, int* prefix,
+                                                float* red, float* part) {
   build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, false);
   const int64_t T = prefix[a.B];
-  const int row = blockIdx.x;
   const int b = row / a.M, m = row - b * a.M;
   const int pb0 = prefix[b], pb1 = prefix[b + 1];
   if (pb1 <= pb0) return;
@@ -865,6 +853,16 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
   // least one page per partition (G <= T) none is empty and the 64-bit divisions
   // that find empty ones are skipped.
   const bool dense = (int64_t)a.G <= T;
+  const int idx = b * a.n_mt + mt;
+  if (a.arrive) {
+    // acquire: one fence invalidates this CU's L1 and the XCD's L2 for all waves, and
+    // the barrier orders it before every wave's reads of the partials
+    if (threadIdx.x == 0) {
+      wait_pieces(a.arrive + idx, pieces_of(T, a.G, g0, g1, dense), a.flags);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+  }
   auto lse_of = [&](int s) {
     const int g = g0 + s;
     if (!dense && part_begin(T, a.G, g) >= part_begin(T, a.G, g + 1)) return -INFINITY;
@@ -922,29 +920,28 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
     accumulate();
   }
 
-  *reinterpret_cast<f32x4*>(&part[pl][8 * cg]) = o0;
-  *reinterpret_cast<f32x4*>(&part[pl][8 * cg + 4]) = o1;
+  *reinterpret_cast<f32x4*>(&part[pl * 512 + 8 * cg]) = o0;
+  *reinterpret_cast<f32x4*>(&part[pl * 512 + 8 * cg + 4]) = o1;
   __syncthreads();
   if (pl == 0) {
 #pragma unroll
     for (int q = 1; q < kCombineLanes; ++q) {
-      o0 += *reinterpret_cast<const f32x4*>(&part[q][8 * cg]);
-      o1 += *reinterpret_cast<const f32x4*>(&part[q][8 * cg + 4]);
+      o0 += *reinterpret_cast<const f32x4*>(&part[q * 512 + 8 * cg]);
+      o1 += *reinterpret_cast<const f32x4*>(&part[q * 512 + 8 * cg + 4]);
     }
     float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * cg;
     *reinterpret_cast<f32x4*>(dst) = o0;
     *reinterpret_cast<f32x4*>(dst + 4) = o1;
     if (cg == 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
   }
+  if (a.arrive && tid == 0) row_merged(a, idx, mt);
 }
 
-// Combine, few pieces per request: one wave per folded query row, four rows per
-// workgroup, no LDS and no barriers.  The wave finds its request's page range by
-// summing the clamped page counts itself, reduces the row's log-sum-exp over the
-// pieces with lane shuffles, and lane l accumulates columns 8 l .. 8 l + 7 over all
-// pieces, four pieces' loads in flight at a time.
-constexpr int kRowsPerCombineGroup = kCombineThreads / 64;
-
+// Few pieces per request: one wave merges folded query row `row`, with no LDS and no
+// barriers.  The wave finds its request's page range by summing the clamped page
+// counts itself, reduces the row's log-sum-exp over the pieces with lane shuffles,
+// and lane l accumulates columns 8 l .. 8 l + 7 over all pieces, four pieces' loads
+// in flight at a time.
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -961,10 +958,8 @@ __device__ __forceinline__ float wave_sumf(float v) {
   return v;
 }
 
-__global__ void __launch_bounds__(kCombineThreads) combine_rows_kernel(CombineArgs a) {
+__device__ __forceinline__ void merge_row_wave(const CombineArgs& a, int64_t row) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerCombineGroup + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.B * a.M) return;  // the whole wave
   const int b = (int)(row / a.M), m = (int)(row - (int64_t)b * a.M);
   int below = 0, total = 0;
   for (int j = lane; j < a.B; j += 64) {
@@ -983,6 +978,11 @@ __global__ void __launch_bounds__(kCombineThreads) combine_rows_kernel(CombineAr
   const int mt = m / a.MT, ml = m - mt * a.MT;
   const int n = g1 - g0 + 1;
   const bool dense = (int64_t)a.G <= T;  // then no partition is empty
+  const int idx = b * a.n_mt + mt;
+  if (a.arrive) {
+    if (lane == 0) wait_pieces(a.arrive + idx, pieces_of(T, a.G, g0, g1, dense), a.flags);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the partials are read after this
+  }
   auto lse_of = [&](int s) {
     const int g = g0 + s;
     if (!dense && part_begin(T, a.G, g) >= part_begin(T, a.G, g + 1)) return -INFINITY;
@@ -1027,12 +1027,144 @@ __global__ void __launch_bounds__(kCombineThreads) combine_rows_kernel(CombineAr
   float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * lane;
   *reinterpret_cast<f32x4*>(dst) = o0;
   *reinterpret_cast<f32x4*>(dst + 4) = o1;
-  if (lane == 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
+  if (lane == 0) {
+    a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
+    if (a.arrive) row_merged(a, idx, mt);
+  }
+}
+
+// The merge arguments of a single-pass call.
+__device__ __forceinline__ CombineArgs merge_args(const SplitArgs& s) {
+  CombineArgs a;
+  a.seq_lens = s.seq_lens;
+  a.O = s.O;
+  a.lse = s.lse;
+  a.part_o = s.part_o;
+  a.part_lse = s.part_lse;
+  a.flags = s.flags;
+  a.arrive = s.arrive;
+  a.done = s.done;
+  a.max_pages = s.max_pages;
+  a.B = s.B;
+  a.Sq = s.Sq;
+  a.H = s.H;
+  a.M = s.M;
+  a.n_mt = s.n_mt;
+  a.G = s.G;
+  a.MT = kMTile;
+  a.slot_rows = s.slot_rows;
+  return a;
+}
+
+// Merging workgroup w of a single-pass call: row w (comb_rows == 0), or rows
+// (4 w + wave) comb_rows .. + comb_rows, one wave each.
+__device__ __forceinline__ void merge_role(const SplitArgs& s, int w, uint8_t* lds) {
+  const CombineArgs a = merge_args(s);
+  if (s.comb_rows == 0) {
+    int* prefix = reinterpret_cast<int*>(lds);
+    float* red = reinterpret_cast<float*>(lds + 8192);
+    float* part = reinterpret_cast<float*>(lds + 8192 + 256);
+    merge_row_group(a, w, prefix, red, part);
+  } else {
+    const int64_t rows = (int64_t)a.B * a.M;
+    const int64_t r0 = ((int64_t)w * kWaves + (threadIdx.x >> 6)) * s.comb_rows;
+    for (int64_t r = r0; r < r0 + s.comb_rows && r < rows; ++r) merge_row_wave(a, r);
+  }
+}
+
+template <class Kv>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+splitkv_kernel(SplitArgs a) {
+  // bf16: 4 x 36 KB ring + 16 KB exchange buffer = the whole 160 KB of LDS;
+  // E4M3: 6 x 20 KB ring + 16 KB
+  __shared__ __attribute__((aligned(16))) uint8_t ring[Kv::kStagesN * Kv::kSlot];
+  __shared__ f32x4 xbuf[kWaves * 4 * 64];  // S^T halves exchanged by wave pairs
+  static_assert(sizeof(f32x4) * kWaves * 4 * 64 >= (2 * kMaxBatch + 1) * sizeof(int),
+                "the page prefix and lengths are built in the exchange buffer");
+
+  if ((int)blockIdx.x >= a.n_split) {  // single pass: a merging workgroup
+    merge_role(a, (int)blockIdx.x - a.n_split, ring);
+    return;
+  }
+  const int lam = xcd_logical_id(blockIdx.x, a.n_split);
+  const int g = lam / a.n_mt;
+  const int mt = lam - g * a.n_mt;
+
+  // page prefix and clamped lengths of the batch, in the exchange buffer until the
+  // first piece starts
+  int* prefix = reinterpret_cast<int*>(xbuf);
+  int* lens = prefix + kMaxBatch + 1;
+  build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, true, lens);
+  const int64_t T = prefix[a.B];
+  const int64_t p0 = part_begin(T, a.G, g);
+  const int64_t p1 = part_begin(T, a.G, g + 1);
+  // first request whose pages reach past p0
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid + 1] > p0) hi = mid; else lo = mid + 1;
+  }
+  int pb0 = prefix[lo];
+  const int L_first = lens[lo];
+  __syncthreads();  // the prefix has been read
+  if (p0 >= p1) return;
+
+  // walk the requests the partition touches; a request's page count is recomputed
+  // from its clamped length (the same count the prefix was built from)
+  for (int b = lo; b < a.B && pb0 < p1; ++b) {
+    const int Lb = b == lo ? L_first : clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
+    const int pb1 = pb0 + (Lb + kPage - 1) / kPage;
+    if (pb1 > pb0) {
+      const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
+      const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
+      const bool whole = plo == 0 && phi == pb1 - pb0;
+      run_piece<Kv>(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
+                    __builtin_amdgcn_readfirstlane(Lb), mt,
+                    __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi),
+                    whole, (b + g) * a.n_mt + mt);
+      if (a.arrive && !whole) {
+        // single pass: every wave's partial stores have reached L2 before the barrier;
+        // one release fence then writes the XCD's L2 back (it covers all four waves)
+        // before the piece is counted
+        wait_vmem_all();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          atomicAdd(a.arrive + b * a.n_mt + mt, 1u);
+        }
+      }
+      __syncthreads();  // LDS free before the next piece stages into it
+    }
+    pb0 = pb1;
+  }
+}
+
+// ---- the separate combine kernels (two-pass calls) ----------------------------------
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
+  __shared__ int prefix[kMaxBatch + 1];
+  __shared__ float red[kCombineLanes];
+  __shared__ __attribute__((aligned(16))) float part[kCombineLanes * 512];
+  merge_row_group(a, blockIdx.x, prefix, red, part);
+}
+
+// four rows per workgroup, one wave each
+constexpr int kRowsPerCombineGroup = kCombineThreads / 64;
+
+__global__ void __launch_bounds__(kCombineThreads) combine_rows_kernel(CombineArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerCombineGroup + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.B * a.M) return;  // the whole wave
+  merge_row_wave(a, row);
 }
 
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream) {
-  const int64_t nwg = (int64_t)a.G * a.n_mt;
-  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t n_split = (int64_t)a.G * a.n_mt;
+  int64_t nwg = n_split;
+  if (a.arrive) {  // single pass: the merging workgroups follow the split-KV ones
+    const int64_t rows = (int64_t)a.B * a.M;
+    const int64_t per = (int64_t)kWaves * a.comb_rows;
+    nwg += a.comb_rows == 0 ? rows : (rows + per - 1) / per;
+  }
+  if (n_split != a.n_split || nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
   if (a.kv_e4m3)
     hipLaunchKernelGGL(splitkv_kernel<E4m3Kv>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   else

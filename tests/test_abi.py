@@ -22,7 +22,8 @@ def test_library_exports_every_header_function():
     names = mla.header_functions()
     assert names == sorted([
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
-        "mla_decode_splitkv", "mla_decode_splitkv_e4m3", "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
+        "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
+        "mla_decode_splitkv_e4m3", "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
         "mla_status_string"])
     L = mla.lib()
     for n in names:
@@ -47,19 +48,32 @@ def test_status_strings():
     assert "unknown" in mla.status_string(12345)
 
 
+def _counters(B, n_mt):
+    """Single-pass arrival + merged-row counters: 2 B n_mt words, in 256-byte units."""
+    return ((2 * B * n_mt * 4 + 255) // 256) * 256
+
+
 def test_workspace_size_explicit_partitions():
-    # one partition: header only; split: (B + G) slots of min(M, 64) rows x (512 + 1) floats
+    # one partition: header only; split: header, counters, then (B + G) slots of
+    # min(M, 64) rows x (512 + 1) floats
     assert mla.workspace_size(4, 4, 16, 1025, 1) == 256
     n = mla.workspace_size(4, 4, 16, 1025, 256)
     slots, rows = (4 + 256) * 1, 64
-    assert n == 256 + slots * rows * 512 * 4 + (((slots * rows * 4) + 255) // 256) * 256
+    assert n == 256 + _counters(4, 1) + slots * rows * 512 * 4 + \
+        (((slots * rows * 4) + 255) // 256) * 256
     # M = 256 rows -> 4 M-tiles of 64 rows
     n2 = mla.workspace_size(16, 16, 16, 3200, 64)
     slots2 = (16 + 64) * 4
-    assert n2 == 256 + slots2 * 64 * 512 * 4 + (((slots2 * 64 * 4) + 255) // 256) * 256
+    assert n2 == 256 + _counters(16, 4) + slots2 * 64 * 512 * 4 + \
+        (((slots2 * 64 * 4) + 255) // 256) * 256
     # M smaller than a tile: slots hold only M rows
     n3 = mla.workspace_size(1, 1, 5, 4, 3)
-    assert n3 == 256 + 4 * 5 * 512 * 4 + 256
+    assert n3 == 256 + _counters(1, 1) + 4 * 5 * 512 * 4 + 256
+    # many M-tiles: the counters span several 256-byte units
+    n4 = mla.workspace_size(64, 4, 128, 100, 2)
+    slots4 = (64 + 2) * 8
+    assert _counters(64, 8) == 4096
+    assert n4 == 256 + 4096 + slots4 * 64 * 512 * 4 + (((slots4 * 64 * 4) + 255) // 256) * 256
 
 
 @pytest.mark.parametrize("args,code", [
@@ -91,7 +105,8 @@ def _call(name="mla_decode", **over):
 
 
 COMPUTE_ENTRY_POINTS = ["mla_decode", "mla_decode_splitkv", "mla_prefill_with_prefix",
-                        "mla_decode_e4m3", "mla_decode_splitkv_e4m3"]
+                        "mla_decode_single_pass", "mla_decode_e4m3", "mla_decode_splitkv_e4m3",
+                        "mla_decode_single_pass_e4m3"]
 
 
 @pytest.mark.parametrize("name", COMPUTE_ENTRY_POINTS)
@@ -111,7 +126,8 @@ def test_compute_entry_points_reject_on_host(name, over, code):
     assert _call(name, **over) == code
 
 
-@pytest.mark.parametrize("name", ["mla_decode_e4m3", "mla_decode_splitkv_e4m3"])
+@pytest.mark.parametrize("name", ["mla_decode_e4m3", "mla_decode_splitkv_e4m3",
+                                  "mla_decode_single_pass_e4m3"])
 @pytest.mark.parametrize("kv_scale", [0.0, -1.0, math.nan, math.inf, -math.inf])
 def test_e4m3_entry_points_reject_bad_scale(name, kv_scale):
     assert _call(name, kv_scale=kv_scale) == INVALID

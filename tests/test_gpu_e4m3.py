@@ -163,6 +163,16 @@ def test_split_and_combine_entry_points_equal_decode():
     assert np.array_equal(O1, O2.cpu().numpy()) and np.array_equal(l1, l2.cpu().numpy())
 
 
+def test_single_pass_equals_two_passes():
+    w = e4m3(seed=233, B=1, Sq=4, H=16, lens=("uniform", 1500, 2500))
+    dev = to_dev(w)
+    for parts in (40, 7):  # a workgroup per merged row, and a wave per row
+        O1, l1 = run(w, parts=parts, dev=dev)
+        O2, l2 = run(w, parts=parts, dev=dev, fn=mla.decode_single_pass_e4m3)
+        assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+        check(O2, l2, *oracle(w), f"single-pass parts={parts}")
+
+
 def test_bound_decode_matches():
     w = e4m3(seed=226, B=2, Sq=4, H=16, lens=("uniform", 600, 1200))
     dev = to_dev(w)

@@ -161,6 +161,17 @@ def test_combine_paths(name, kw, later, parts):
     check(O, lse, *oracle(w), name)
 
 
+@pytest.mark.parametrize("name,kw,later,parts", COMBINE_CASES, ids=[c[0] for c in COMBINE_CASES])
+def test_single_pass_merge_paths(name, kw, later, parts):
+    """The combine cases (both merge forms, long and empty partitions, shortened
+    requests) through the one-launch entry point."""
+    w = make_workload("tiny", **kw)
+    if later is not None:
+        w = _shorten(w, later)
+    O, lse = run(w, parts=parts, fn=mla.decode_single_pass)
+    check(O, lse, *oracle(w), name + " single-pass")
+
+
 def test_split_and_combine_entry_points_equal_decode():
     w = make_workload("tiny", seed=113, B=2, Sq=4, H=16, lens=("uniform", 600, 1200))
     dev = to_dev(w)
@@ -171,6 +182,56 @@ def test_split_and_combine_entry_points_equal_decode():
     mla.decode_combine(dev["seq_lens"], w.max_pages, w.Sq, w.H, O2, l2, ws, 9)
     torch.cuda.synchronize()
     assert np.array_equal(O1, O2.cpu().numpy()) and np.array_equal(l1, l2.cpu().numpy())
+
+
+@pytest.mark.parametrize("B,parts", [(1, 40), (3, 7)], ids=["merge-per-workgroup", "merge-per-wave"])
+def test_single_pass_equals_two_passes(B, parts):
+    """mla_decode_single_pass (one launch, merging workgroups appended to the split grid)
+    gives the two-pass result bit for bit, in both merge forms (G >= 16 B and G < 16 B)."""
+    w = make_workload("tiny", seed=130 + B, B=B, Sq=4, H=16, lens=("uniform", 900, 2500))
+    dev = to_dev(w)
+    ws = mla.new_workspace(w.B, w.Sq, w.H, w.max_pages, parts)
+    O1, l1 = mla.decode_single_pass(dev["q_nope"], dev["q_rope"], dev["kv_pool"],
+                                    dev["block_table"], dev["seq_lens"], float(w.scale), True,
+                                    parts, workspace=ws)
+    O2, l2 = mla.decode_splitkv(dev["q_nope"], dev["q_rope"], dev["kv_pool"], dev["block_table"],
+                                dev["seq_lens"], float(w.scale), True, parts, workspace=ws)
+    mla.decode_combine(dev["seq_lens"], w.max_pages, w.Sq, w.H, O2, l2, ws, parts)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+    check(O1.cpu().numpy().astype(np.float64), l1.cpu().numpy().astype(np.float64), *oracle(w),
+          f"single-pass B={B} parts={parts}")
+    assert mla.read_error_flags(ws) == 0
+
+
+def _counter_words(ws, B, n_mt):
+    """The single-pass counters (arrive, then merged rows) after the 256-byte header."""
+    return ws[256:256 + 8 * B * n_mt].view(torch.int32).cpu().numpy()
+
+
+def test_single_pass_counters_return_to_zero_and_workspace_is_reusable():
+    """Every single-pass call leaves its counters at zero, so one workspace serves calls
+    of other shapes and partition counts, in both merge forms, back to back."""
+    shapes = [
+        (make_workload("tiny", seed=140, B=2, Sq=4, H=16, lens=("uniform", 1500, 2600)), 48),
+        (make_workload("tiny", seed=141, B=3, Sq=8, H=16, lens=("uniform", 700, 1400)), 5),
+        (make_workload("tiny", seed=142, B=1, Sq=2, H=16, lens=("fixed", 150)), 11),  # G > pages
+    ]
+    need = max(mla.workspace_size(w.B, w.Sq, w.H, w.max_pages, g) for w, g in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    refs = [oracle(w) for w, _ in shapes]
+    devs = [to_dev(w) for w, _ in shapes]
+    for rnd in range(2):
+        for (w, g), ref, dev in zip(shapes, refs, devs):
+            O, lse = mla.decode_single_pass(dev["q_nope"], dev["q_rope"], dev["kv_pool"],
+                                            dev["block_table"], dev["seq_lens"], float(w.scale),
+                                            True, g, workspace=ws)
+            torch.cuda.synchronize()
+            n_mt = (w.Sq * w.H + 63) // 64
+            assert not _counter_words(ws, w.B, n_mt).any(), f"counters left set (round {rnd})"
+            check(O.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), *ref,
+                  f"reuse round {rnd} B={w.B} G={g}")
+    assert mla.read_error_flags(ws) == 0
 
 
 def test_prefill_entry_point_small():
