@@ -11,11 +11,12 @@ like the pages' coding-agent workloads.
 Prints one JSON line.  `value` is KV-read throughput: the latent bytes a step must
 read (every visible row once, 576 bf16) divided by the measured time per step.
 `roofline` rates the dominant kernel (the split-KV pass) against its MI355X peak.
-Its duration is measured with HIP events on the stream the kernels run on, around
-a run of back-to-back split launches over the same pool rotation after the timed
-steps.  Per-launch split durations (from a separate run of the steps with an event
-pair around each split launch) are reported too; they also count each launch's
-dispatch and end-of-kernel release.  Its `traffic` is the HBM bytes per
+Its duration is the average of per-launch HIP event pairs recorded around each
+split launch on the stream the kernels run on, in a second run of the same steps
+(the timed steps themselves carry no event markers); like rocprofv3's kernel
+durations, they include each launch's dispatch and end-of-kernel release.  A run of
+back-to-back split launches, where those overlap the neighbouring launches, is
+reported too.  Its `traffic` is the HBM bytes per
 launch measured by rocprofv3 counters (stored under profiles/ and used only while
 the kernel sources are unchanged).  `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
@@ -122,6 +123,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies cycled per step (0 = enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-pass", action="store_true",
+                    help="skip the one-launch comparison (profiler runs: every split-KV kernel "
+                         "launch is then a split pass alone)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, launch a plain 256 MiB device copy 3 times (counter "
                          "calibration for rocprofv3 --pmc runs)")
@@ -222,7 +226,7 @@ def main():
 
     # The same steps in one launch each (mla_decode_single_pass), for comparison.
     single_pass_us = None
-    if G > 1:
+    if G > 1 and not args.no_single_pass:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -242,8 +246,9 @@ def main():
         del src, dst
 
     value = work["kv_bytes"] / (ms_step * 1e-3) / 1e9
-    hbm_achieved = work["bytes"] / (split_b2b * 1e-3) / 1e9
-    mfma_achieved = work["flops"] / (split_b2b * 1e-3) / 1e12
+    # the dominant kernel's average launch duration: per-launch events on its stream
+    hbm_achieved = work["bytes"] / (split_avg * 1e-3) / 1e9
+    mfma_achieved = work["flops"] / (split_avg * 1e-3) / 1e12
     traffic = stored_traffic(args.config, args.kv)
     # the bound is the roof the step's arithmetic intensity meets first
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
