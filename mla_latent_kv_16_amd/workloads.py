@@ -256,3 +256,32 @@ def kv_bytes_expected(spec: WorkloadSpec) -> float:
 
 def pages_for(L: int) -> int:
     return int(math.ceil(L / PAGE))
+
+
+def make_tree_masks(B: int, Sq: int, kind: str = "random", seed: int = 0) -> np.ndarray:
+    """Draft trees as ancestor bit masks, uint64 [B, Sq] (Sq <= 64).
+
+    Bit u of mask[b, t] marks draft u as an ancestor of draft t (or t itself).
+    Drafts are numbered parents first.  kind: "chain" (draft t's parent is t - 1),
+    "star" (every draft hangs off the cached prefix) or "random" (each draft t > 0
+    picks its parent uniformly among the prefix and drafts 0 .. t - 1, seeded).
+    """
+    if not 1 <= Sq <= 64:
+        raise ValueError("tree drafts need 1 <= Sq <= 64")
+    rng = np.random.default_rng(seed)
+    masks = np.zeros((B, Sq), dtype=np.uint64)
+    for b in range(B):
+        anc = []
+        for t in range(Sq):
+            if kind == "chain":
+                parent = t - 1
+            elif kind == "star":
+                parent = -1
+            elif kind == "random":
+                parent = int(rng.integers(-1, t)) if t > 0 else -1
+            else:
+                raise ValueError(kind)
+            m = (1 << t) | (anc[parent] if parent >= 0 else 0)
+            anc.append(m)
+            masks[b, t] = np.uint64(m)
+    return masks

@@ -15,4 +15,7 @@ from .mla_oracle import (  # noqa: F401
     mla_attention_rows,
     lse_merge,
     mla_attention_pages,
+    tree_visible,
+    mla_attention_tree,
+    mla_attention_tree_loop,
 )

@@ -44,6 +44,10 @@ Definition (for b < B, t < Sq, h < H):
   LSE      = log(sum_{j < n_vis} exp(s_j))
   O[b,t,h] = sum_{j < n_vis} exp(s_j - LSE) * K_b[j][:512]
 
+Tree-shaped drafts (tree_visible, mla_attention_tree[_loop]) replace the causal
+chain among the drafts by each draft's ancestor set; their pins live in
+tests/test_oracle_tree.py.
+
 Parity pins for every function here live in tests/test_oracle.py (brute-force
 unabsorbed MLA, fold identity, normalisation, single-row and uniform closed
 forms, causal = sequential decodes, paging invariance, dense SDPA special case,
@@ -244,6 +248,67 @@ def mla_attention_pages(q_nope, q_rope, pool, block_table, seq_lens, scale, caus
             O[t, h] = np.exp(s - lse) @ kv[:, :NOPE]
             LSE[t, h] = lse
     return O, LSE
+
+
+def tree_visible(L: int, Sq: int, t: int, mask_word: int) -> np.ndarray:
+    """Rows draft t sees under a draft tree: the cached prefix rows 0 .. L-Sq-1, then
+    the draft rows L-Sq+t' for every t' <= t whose bit t' is set in mask_word, and
+    always its own row L-Sq+t.
+
+    Drafts of a tree are verified in parallel, each against its own branch (atlas
+    §16 Speculative decoding; the atlas node on tree-shaped drafts).  Reading: drafts
+    are numbered so that every ancestor precedes its descendants, bit t' of a
+    draft's mask word marks ancestor t', bits above t are ignored, and a draft always
+    sees itself.
+    """
+    prefix = np.arange(L - Sq)
+    own = [L - Sq + u for u in range(t + 1) if u == t or (int(mask_word) >> u) & 1]
+    return np.concatenate([prefix, np.asarray(own, dtype=np.int64)])
+
+
+def mla_attention_tree_loop(q_nope, q_rope, pool, block_table, seq_lens, scale, tree_mask):
+    """Tree-masked attention, explicit loop over (request, draft, head): each query
+    attends to exactly the rows tree_visible() lists.  tree_mask: uint64 [B, Sq].
+    Returns fp64 (O [B,Sq,H,512], LSE [B,Sq,H]).  Meant for small inputs."""
+    B, Sq, H = q_nope.shape[:3]
+    scale = float(scale)
+    O = np.zeros((B, Sq, H, NOPE))
+    LSE = np.zeros((B, Sq, H))
+    for b in range(B):
+        L = int(seq_lens[b])
+        rows = gather_latent_rows(pool, block_table, b, L)
+        for t in range(Sq):
+            kv = rows[tree_visible(L, Sq, t, int(tree_mask[b, t]))]
+            for h in range(H):
+                qn, qr = _query_rows(q_nope, q_rope, b, t, h)
+                s = scale * (kv[:, :NOPE] @ qn + kv[:, NOPE:] @ qr)
+                mx = s.max()
+                lse = mx + np.log(np.exp(s - mx).sum())
+                O[b, t, h] = np.exp(s - lse) @ kv[:, :NOPE]
+                LSE[b, t, h] = lse
+    return O, LSE
+
+
+def mla_attention_tree(q_nope, q_rope, pool, block_table, seq_lens, scale, tree_mask):
+    """Tree-masked attention in the folded form: per request one [Sq*H, 576] x [576, L]
+    product with each folded row m = t*H + h masked to tree_visible(L, Sq, t, ...)."""
+    B, Sq, H = q_nope.shape[:3]
+    M = Sq * H
+    O = np.zeros((B, M, NOPE))
+    LSE = np.zeros((B, M))
+    for b in range(B):
+        L = int(seq_lens[b])
+        rows = gather_latent_rows(pool, block_table, b, L)
+        Q = _folded_rows(q_nope, q_rope, b)
+        vis = np.zeros((Sq, L), dtype=bool)
+        for t in range(Sq):
+            vis[t, tree_visible(L, Sq, t, int(tree_mask[b, t]))] = True
+        S = (Q @ rows.T) * float(scale)
+        S = np.where(np.repeat(vis, H, axis=0), S, -np.inf)
+        mx = S.max(axis=1, keepdims=True)
+        LSE[b] = mx[:, 0] + np.log(np.exp(S - mx).sum(axis=1))
+        O[b] = np.exp(S - LSE[b][:, None]) @ rows[:, :NOPE]
+    return O.reshape(B, Sq, H, NOPE), LSE.reshape(B, Sq, H)
 
 
 def lse_merge(parts):
