@@ -214,6 +214,33 @@ int mla_decode_single_pass_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
                                 void* stream);
 
 /*
+ * Decode of a draft TREE (atlas §16 Speculative decoding: candidates are verified
+ * in parallel, EAGLE-2 building them as a tree; the atlas node on tree-shaped
+ * drafts).  The Sq drafts of a request are numbered parents first and occupy its
+ * last Sq rows as in mla_decode; draft t sees the cached prefix (rows < L_b - Sq),
+ * its own row L_b - Sq + t, and row L_b - Sq + u for every u < t whose bit u is set
+ * in tree_mask[b * Sq + t] (its ancestors).  Bits above t are ignored.  A chain
+ * (bits 0..t set) is exactly mla_decode with causal = 1.
+ *
+ *   tree_mask  uint64 [B, Sq], 8-byte aligned device memory; 1 <= Sq <= 64
+ *              (Sq > 64: MLA_ERR_UNSUPPORTED)
+ *
+ * Every other argument is as for mla_decode (there is no causal flag); the E4M3
+ * variant takes the pool and its scale as mla_decode_e4m3 does.
+ */
+int mla_decode_tree(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                    int64_t num_pages, int page_size, const int32_t* block_table,
+                    int max_pages_per_seq, const int32_t* seq_lens, const uint64_t* tree_mask,
+                    int B, int Sq, int H, float softmax_scale, int num_partitions, float* O,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+int mla_decode_tree_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* kv_pool,
+                         float kv_scale, int64_t num_pages, int page_size,
+                         const int32_t* block_table, int max_pages_per_seq,
+                         const int32_t* seq_lens, const uint64_t* tree_mask, int B, int Sq,
+                         int H, float softmax_scale, int num_partitions, float* O, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Waits for `stream`, then copies the workspace header's error flags
  * (MLA_FLAG_*) to *flags and clears them.  Reading forces a synchronisation, so
  * callers use it in checked runs and tests, not on the hot path.

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     decode_single_pass_e4m3,
     decode_splitkv,
     decode_splitkv_e4m3,
+    decode_tree,
     header_functions,
     lib,
     new_workspace,

@@ -47,6 +47,10 @@ _SIGNATURES = {
     "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
     "mla_decode_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_single_pass": (_COMPUTE_ARGS, _i32),
+    "mla_decode_tree": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
+                         _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "mla_decode_tree_e4m3": ([_vp, _vp, _vp, _f32, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
+                              _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_single_pass_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_splitkv_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_combine": ([_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -243,6 +247,35 @@ def decode_single_pass(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_s
     to the split-KV grid)."""
     return _compute("mla_decode_single_pass", q_nope, q_rope, kv_pool, block_table, seq_lens,
                     softmax_scale, causal, num_partitions, out, lse, workspace, stream)
+
+
+def _tree_mask_arg(tree_mask, B, Sq):
+    torch = _torch()
+    if tree_mask.dtype not in (torch.int64, torch.uint64) or tuple(tree_mask.shape) != (B, Sq):
+        raise ValueError("tree_mask must be int64/uint64 [B, Sq] (ancestor bits)")
+    if not tree_mask.is_contiguous() or not tree_mask.is_cuda:
+        raise ValueError("tree_mask must be a contiguous device tensor")
+    return _ptr(tree_mask)
+
+
+def decode_tree(q_nope, q_rope, kv_pool, block_table, seq_lens, tree_mask, softmax_scale,
+                num_partitions=0, out=None, lse=None, workspace=None, stream=None,
+                kv_scale=None):
+    """mla_decode_tree (bf16 pool) or mla_decode_tree_e4m3 (uint8 pool with kv_scale):
+    decode of a draft tree, tree_mask int64 [B, Sq] ancestor bits (Sq <= 64)."""
+    e4m3 = kv_scale is not None
+    B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table, seq_lens,
+                                                out, lse, workspace, num_partitions, e4m3=e4m3)
+    tm = _tree_mask_arg(tree_mask, B, Sq)
+    L = lib()
+    pool = (_ptr(kv_pool), float(kv_scale)) if e4m3 else (_ptr(kv_pool),)
+    name = "mla_decode_tree_e4m3" if e4m3 else "mla_decode_tree"
+    st = getattr(L, name)(_ptr(q_nope), _ptr(q_rope), *pool, kv_pool.shape[0], PAGE_SIZE,
+                          _ptr(block_table), maxp, _ptr(seq_lens), tm, B, Sq, H,
+                          float(softmax_scale), int(num_partitions), _ptr(out), _ptr(lse),
+                          _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(st, name)
+    return out, lse
 
 
 def decode_splitkv(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,

@@ -150,10 +150,11 @@ int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool,
 
 int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
                   const void* kv_pool, int kv_e4m3, float kv_scale, int64_t num_pages,
-                  const int32_t* block_table, int max_pages, const int32_t* seq_lens, int B,
-                  int Sq, int H, float scale, int causal, float* O, float* lse,
-                  bool single_pass, hipStream_t stream) {
+                  const int32_t* block_table, int max_pages, const int32_t* seq_lens,
+                  const uint64_t* tree_mask, int B, int Sq, int H, float scale, int causal,
+                  float* O, float* lse, bool single_pass, hipStream_t stream) {
   SplitArgs a;
+  a.tree_mask = tree_mask;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
   a.kv_pool = kv_pool;
@@ -227,7 +228,8 @@ int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_p
                 float kv_scale, int64_t num_pages, int page_size, const int32_t* block_table,
                 int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
                 float softmax_scale, int causal, int num_partitions, float* O, float* lse,
-                void* workspace, size_t workspace_bytes, void* stream, bool single_pass) {
+                void* workspace, size_t workspace_bytes, void* stream, bool single_pass,
+                const uint64_t* tree_mask = nullptr) {
   if (kv_e4m3 && (!(kv_scale > 0.0f) || isinf(kv_scale))) return MLA_ERR_INVALID_ARG;
   Call c;
   int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
@@ -236,8 +238,8 @@ int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_p
   if (st != MLA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = enqueue_split(c, q_nope, q_rope, kv_pool, kv_e4m3, kv_scale, num_pages, block_table,
-                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
-                     single_pass, s);
+                     max_pages_per_seq, seq_lens, tree_mask, B, Sq, H, softmax_scale, causal, O,
+                     lse, single_pass, s);
   if (st != MLA_OK || single_pass) return st;
   return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
 }
@@ -289,8 +291,8 @@ int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uin
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
   return enqueue_split(c, q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
-                       false, static_cast<hipStream_t>(stream));
+                       max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
+                       lse, false, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_combine(const int32_t* seq_lens, int max_pages_per_seq, int B, int Sq, int H,
@@ -355,8 +357,8 @@ int mla_decode_splitkv_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
   return enqueue_split(c, q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, O, lse,
-                       false, static_cast<hipStream_t>(stream));
+                       max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
+                       lse, false, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* kv_pool,
@@ -379,6 +381,31 @@ int mla_decode_single_pass_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
   return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
                      num_partitions, O, lse, workspace, workspace_bytes, stream, true);
+}
+
+int mla_decode_tree(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                    int64_t num_pages, int page_size, const int32_t* block_table,
+                    int max_pages_per_seq, const int32_t* seq_lens, const uint64_t* tree_mask,
+                    int B, int Sq, int H, float softmax_scale, int num_partitions, float* O,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!tree_mask || (reinterpret_cast<uintptr_t>(tree_mask) & 7)) return MLA_ERR_INVALID_ARG;
+  if (Sq > 64) return MLA_ERR_UNSUPPORTED;
+  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1, num_partitions, O,
+                     lse, workspace, workspace_bytes, stream, false, tree_mask);
+}
+
+int mla_decode_tree_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* kv_pool,
+                         float kv_scale, int64_t num_pages, int page_size,
+                         const int32_t* block_table, int max_pages_per_seq,
+                         const int32_t* seq_lens, const uint64_t* tree_mask, int B, int Sq,
+                         int H, float softmax_scale, int num_partitions, float* O, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!tree_mask || (reinterpret_cast<uintptr_t>(tree_mask) & 7)) return MLA_ERR_INVALID_ARG;
+  if (Sq > 64) return MLA_ERR_UNSUPPORTED;
+  return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1, num_partitions, O,
+                     lse, workspace, workspace_bytes, stream, false, tree_mask);
 }
 
 int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {

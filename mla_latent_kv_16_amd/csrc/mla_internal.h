@@ -13,6 +13,7 @@ struct SplitArgs {
   const void* kv_pool;         // [num_pages, 64, 576] bf16, or E4M3 codes when kv_e4m3
   const int32_t* block_table;  // [B, max_pages]
   const int32_t* seq_lens;     // [B]
+  const uint64_t* tree_mask;   // [B, Sq] draft-tree ancestor bits, or nullptr (a chain)
   float* O;                    // [B, M, 512]
   float* lse;                  // [B, M]  natural log
   float* part_o;               // [slots, slot_rows, 512]  normalised partial outputs

@@ -424,13 +424,16 @@ __device__ __forceinline__ void store_partial(f32x4* xs, const f32x16& s) {
 // `partner` the other wave's half in LDS.  When HAS_NEXT, this wave's half of block
 // i + 1 replaces s_own and its copy in `own` (read by the partner), after a
 // workgroup barrier that follows every wave's reads of block i's halves.  `lim` is
-// the number of leading rows of block i this lane's query row may see.
+// the number of leading rows of block i this lane's query row may see; with a draft
+// tree, rows from `drow0` on are draft rows (row drow0 + u is draft u), seen only
+// where bit u of `tm` is set (drow0 >= 32 when the block holds no draft row).
 template <bool HAS_NEXT, class Kv>
 __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk_next,
                                           const typename Kv::Bases& rb, const bf16x8* qreg,
                                           f32x16& s_own, f32x4* own, const f32x4* partner,
-                                          WaveState& ws, int lim, float scale_log2,
-                                          const CopyJob& job, const typename Kv::Offsets& so) {
+                                          WaveState& ws, int lim, int drow0, uint64_t tm,
+                                          float scale_log2, const CopyJob& job,
+                                          const typename Kv::Offsets& so) {
   const int lane = threadIdx.x & 63;
   constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
 
@@ -463,10 +466,15 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[4 * j + e] = s_own[4 * j + e] + pr[j][e];
     } else if (kk == 2) {
-      if (__builtin_amdgcn_ballot_w64(lim < kKvBlock)) {
+      if (__builtin_amdgcn_ballot_w64(lim < kKvBlock || drow0 < kKvBlock)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (acc_row(lane, i) >= lim) x[i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          // branch-free: row r is seen if r < lim and, for a draft row, its bit is set
+          const int r = acc_row(lane, i);
+          const uint32_t bit = (uint32_t)(tm >> ((r - drow0) & 63)) & 1u;
+          const uint32_t ok = (uint32_t)(r < lim) & ((uint32_t)(r < drow0) | bit);
+          x[i] = ok ? x[i] : -INFINITY;
+        }
       }
     } else if (kk == 4) {
       // row max (a query row's 32 scores sit in lanes l and l + 32), in the log2
@@ -612,16 +620,20 @@ __device__ __forceinline__ const uint8_t* block_source(const SplitArgs& a, PageI
 }
 
 // Waits until at most `sets` blocks' worth of this wave's copies are in flight
-// (copies complete in issue order; sets = 0..4).
-template <int kCopies>
+// (copies complete in issue order; sets = 0..kMax, larger counts wait for kMax).
+template <int kCopies, int kMax>
 __device__ __forceinline__ void wait_copy_sets(int sets) {
-  static_assert(kCopies * 4 <= 63, "vmcnt immediate");
-  switch (sets) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies) : "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kCopies) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kCopies) : "memory"); break;
+  static_assert(kCopies * kMax <= 63 && kMax >= 1 && kMax <= 4, "vmcnt immediate");
+  if (sets <= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else if (kMax == 1 || sets == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");
+  } else if (kMax == 2 || sets == 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies) : "memory");
+  } else if (kMax == 3 || sets == 3) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kCopies) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kCopies) : "memory");
   }
 }
 
@@ -676,6 +688,18 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   f32x4* own = xbuf + wave * 4 * 64;  // this wave's S^T half (4 x 64 lanes x f32x4)
   const f32x4* partner = xbuf + (wave ^ 1) * 4 * 64;
   auto lim_of = [&](int i) { return n_vis - (lo + (i >> 1)) * kPage - (i & 1) * kKvBlock; };
+  // draft tree: this lane's ancestor bits (bits above its own draft ignored, its own
+  // bit always set) and the block row where draft 0 sits
+  uint64_t tm = 0;
+  int d_first = 1 << 30;  // no tree: no block holds draft rows
+  if (a.tree_mask) {
+    d_first = L - a.Sq;
+    if (q_ok) tm = (a.tree_mask[(size_t)b * a.Sq + t] & ((2ull << t) - 1ull)) | (1ull << t);
+  }
+  auto drow_of = [&](int i) {
+    const int r = d_first - (lo + (i >> 1)) * kPage - (i & 1) * kKvBlock;
+    return a.tree_mask ? r : (1 << 30);
+  };
   // copy sets issued after block i + 1's when iteration i starts: the prologue's
   // later blocks plus one set per step (a tail block copied at an iteration's top
   // only adds to that count)
@@ -705,7 +729,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
         Kv::stage(srcs[j], ring_slot<Kv>(ring, j), valid, so);
       }
     }
-    wait_copy_sets<Kv::kCopies>(min(nb, AHEAD) - 1);  // block 0 has landed
+    wait_copy_sets<Kv::kCopies, AHEAD - 1>(min(nb, AHEAD) - 1);  // block 0 has landed
     __syncthreads();
     f32x16 s_own = {};  // this wave's half of S^T of the block being scored
     if (nb > 0) {
@@ -714,7 +738,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     }
     int i = 0;
     for (; i + 1 < nb; ++i) {
-      wait_copy_sets<Kv::kCopies>(sets_after);  // block i + 1 has landed ...
+      wait_copy_sets<Kv::kCopies, AHEAD - 2>(sets_after);  // block i + 1 has landed ...
       // ... in every wave; both S^T halves of block i are in LDS; every wave is done
       // with block i - 1, whose slot now receives block i + AHEAD
       __syncthreads();
@@ -729,7 +753,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
           Kv::stage(src_new, ring_slot<Kv>(ring, i + AHEAD), valid, so);
       }
       pipe_step<true, Kv>(ring_slot<Kv>(ring, i), ring_slot<Kv>(ring, i + 1), rb, qreg, s_own,
-                          own, partner, ws, lim_of(i), a.scale_log2, job, so);
+                          own, partner, ws, lim_of(i), drow_of(i), tm, a.scale_log2, job, so);
 #pragma unroll
       for (int j = 0; j + 1 < AHEAD; ++j) srcs[j] = srcs[j + 1];
       srcs[AHEAD - 1] = src_new;
@@ -737,7 +761,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     if (i < nb) {  // the last block (already in LDS): nothing left to score ahead or copy
       __syncthreads();
       pipe_step<false, Kv>(ring_slot<Kv>(ring, i), nullptr, rb, qreg, s_own, own, partner, ws,
-                           lim_of(i), a.scale_log2, CopyJob{}, so);
+                           lim_of(i), drow_of(i), tm, a.scale_log2, CopyJob{}, so);
     }
     // a row whose scores outgrew its reference by more than the lazy bound forces a
     // second pass for the whole workgroup; the flag lives in the exchange buffer

@@ -18,4 +18,5 @@ from .mla_oracle import (  # noqa: F401
     tree_visible,
     mla_attention_tree,
     mla_attention_tree_loop,
+    mla_attention_tree_rows,
 )

@@ -311,6 +311,25 @@ def mla_attention_tree(q_nope, q_rope, pool, block_table, seq_lens, scale, tree_
     return O.reshape(B, Sq, H, NOPE), LSE.reshape(B, Sq, H)
 
 
+def mla_attention_tree_rows(q_nope, q_rope, pool, block_table, seq_lens, scale, tree_mask, b,
+                            m_list):
+    """Folded rows ``m_list`` (m = t*H + h) of request b under a draft tree:
+    (O [n,512], LSE [n]), each row attending to tree_visible() of its draft."""
+    Sq, H = q_nope.shape[1:3]
+    L = int(seq_lens[b])
+    rows = gather_latent_rows(pool, block_table, b, L)
+    Q = _folded_rows(q_nope, q_rope, b)
+    O = np.zeros((len(m_list), NOPE))
+    LSE = np.zeros(len(m_list))
+    for k, m in enumerate(m_list):
+        kv = rows[tree_visible(L, Sq, int(m) // H, int(tree_mask[b, int(m) // H]))]
+        s = (kv @ Q[int(m)]) * float(scale)
+        mx = s.max()
+        LSE[k] = mx + np.log(np.exp(s - mx).sum())
+        O[k] = np.exp(s - LSE[k]) @ kv[:, :NOPE]
+    return O, LSE
+
+
 def lse_merge(parts):
     """Merge split partials [(O_s, LSE_s), ...] into (O, LSE).
 

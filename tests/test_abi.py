@@ -23,7 +23,8 @@ def test_library_exports_every_header_function():
     assert names == sorted([
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
-        "mla_decode_splitkv_e4m3", "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
+        "mla_decode_splitkv_e4m3", "mla_decode_tree", "mla_decode_tree_e4m3",
+        "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
         "mla_status_string"])
     L = mla.lib()
     for n in names:
@@ -131,6 +132,33 @@ def test_compute_entry_points_reject_on_host(name, over, code):
 @pytest.mark.parametrize("kv_scale", [0.0, -1.0, math.nan, math.inf, -math.inf])
 def test_e4m3_entry_points_reject_bad_scale(name, kv_scale):
     assert _call(name, kv_scale=kv_scale) == INVALID
+
+
+def _tree_call(name="mla_decode_tree", **over):
+    a = dict(q_nope=FAKE, q_rope=FAKE, kv_pool=FAKE, num_pages=8, page_size=64,
+             block_table=FAKE, max_pages=4, seq_lens=FAKE, tree=FAKE, B=1, Sq=4, H=16,
+             scale=0.07, parts=2, O=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None,
+             kv_scale=0.015625)
+    a.update(over)
+    pool = ((a["kv_pool"], a["kv_scale"]) if name.endswith("_e4m3") else (a["kv_pool"],))
+    return getattr(mla.lib(), name)(
+        a["q_nope"], a["q_rope"], *pool, a["num_pages"], a["page_size"], a["block_table"],
+        a["max_pages"], a["seq_lens"], a["tree"], a["B"], a["Sq"], a["H"], a["scale"], a["parts"],
+        a["O"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["mla_decode_tree", "mla_decode_tree_e4m3"])
+@pytest.mark.parametrize("over,code", [
+    (dict(tree=None), INVALID), (dict(tree=FAKE + 4), INVALID), (dict(Sq=65), UNSUPPORTED),
+    (dict(Sq=0), INVALID), (dict(q_nope=None), INVALID), (dict(page_size=32), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(scale=math.nan), INVALID),
+])
+def test_tree_entry_points_reject_on_host(name, over, code):
+    assert _tree_call(name, **over) == code
+
+
+def test_tree_e4m3_rejects_bad_scale():
+    assert _tree_call("mla_decode_tree_e4m3", kv_scale=0.0) == INVALID
 
 
 def test_workspace_one_byte_short_is_rejected():

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import (mla_attention_folded, mla_attention_loop, mla_attention_tree,
-                    mla_attention_tree_loop, tree_visible)
+                    mla_attention_tree_loop, mla_attention_tree_rows, tree_visible)
 from mla_latent_kv_16_amd.workloads import PAGE, make_tree_masks, make_workload
 
 
@@ -105,3 +105,15 @@ def test_tree_mask_generator_structure():
                     assert int(m[b, u]) & ~v == 0
     assert (make_tree_masks(1, 5, "chain") == np.array([[1, 3, 7, 15, 31]], dtype=np.uint64)).all()
     assert (make_tree_masks(1, 4, "star") == np.array([[1, 2, 4, 8]], dtype=np.uint64)).all()
+
+
+def test_tree_rows_form_matches_folded_form():
+    w = small(307, B=2, Sq=8, H=3)
+    masks = make_tree_masks(w.B, w.Sq, "random", seed=5)
+    O, l = mla_attention_tree(w.q_nope, w.q_rope, w.kv_pool, w.block_table, w.seq_lens, w.scale,
+                              masks)
+    ms = [0, 5, 11, 23]
+    o, ll = mla_attention_tree_rows(w.q_nope, w.q_rope, w.kv_pool, w.block_table, w.seq_lens,
+                                    w.scale, masks, 1, ms)
+    assert np.allclose(o, O[1].reshape(-1, 512)[ms], atol=1e-12)
+    assert np.allclose(ll, l[1].reshape(-1)[ms], atol=1e-12)
