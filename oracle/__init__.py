@@ -19,4 +19,5 @@ from .mla_oracle import (  # noqa: F401
     mla_attention_tree,
     mla_attention_tree_loop,
     mla_attention_tree_rows,
+    mla_attention_varlen,
 )

@@ -330,6 +330,28 @@ def mla_attention_tree_rows(q_nope, q_rope, pool, block_table, seq_lens, scale, 
     return O, LSE
 
 
+def mla_attention_varlen(q_nope, q_rope, pool, block_table, seq_lens, scale, q_lens):
+    """Per-request draft counts: request b verifies q_lens[b] <= Sq drafts, which
+    are its last q_lens[b] rows; draft t < q_lens[b] sees rows j <= L_b - q_lens[b] + t.
+    Query slots t >= q_lens[b] are padding and see nothing: O = 0, LSE = -inf.
+
+    Speculative decoding verifies a varying number of candidates per request (atlas
+    §16 Speculative decoding: longer drafts are not always faster); the reading is
+    that a batch pads its queries to the largest count.  Returns fp64
+    (O [B,Sq,H,512], LSE [B,Sq,H])."""
+    B, Sq, H = q_nope.shape[:3]
+    O = np.zeros((B, Sq, H, NOPE))
+    LSE = np.full((B, Sq, H), -np.inf)
+    for b in range(B):
+        n = int(q_lens[b])
+        if n < 1:
+            continue
+        o, l = mla_attention_folded(q_nope[b:b + 1, :n], q_rope[b:b + 1, :n], pool,
+                                    block_table[b:b + 1], seq_lens[b:b + 1], scale, True)
+        O[b, :n], LSE[b, :n] = o[0], l[0]
+    return O, LSE
+
+
 def lse_merge(parts):
     """Merge split partials [(O_s, LSE_s), ...] into (O, LSE).
 
