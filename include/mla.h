@@ -241,6 +241,25 @@ int mla_decode_tree_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const u
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode with a per-request number of drafts (atlas §16 Speculative decoding: the
+ * number of candidates verified per request varies).  Request b verifies
+ * q_lens[b] drafts, 1 <= q_lens[b] <= min(Sq, L_b), held in its first q_lens[b]
+ * query slots and its last q_lens[b] cached rows, each draft t seeing rows
+ * j <= L_b - q_lens[b] + t.  Query slots t >= q_lens[b] are padding: their O rows
+ * are 0 and their LSE is -inf.  A q_lens entry out of range is clamped and raises
+ * MLA_FLAG_BAD_SEQ_LEN.  seq_lens[b] must be at least q_lens[b] (not Sq).
+ *
+ *   q_lens  int32 [B], 4-byte aligned device memory
+ *
+ * Every other argument is as for mla_decode with causal = 1.
+ */
+int mla_decode_varlen(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                      int64_t num_pages, int page_size, const int32_t* block_table,
+                      int max_pages_per_seq, const int32_t* seq_lens, const int32_t* q_lens,
+                      int B, int Sq, int H, float softmax_scale, int num_partitions, float* O,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Waits for `stream`, then copies the workspace header's error flags
  * (MLA_FLAG_*) to *flags and clears them.  Reading forces a synchronisation, so
  * callers use it in checked runs and tests, not on the hot path.

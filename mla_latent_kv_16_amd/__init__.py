@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     decode_splitkv,
     decode_splitkv_e4m3,
     decode_tree,
+    decode_varlen,
     header_functions,
     lib,
     new_workspace,

@@ -47,6 +47,8 @@ _SIGNATURES = {
     "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
     "mla_decode_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_single_pass": (_COMPUTE_ARGS, _i32),
+    "mla_decode_varlen": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
+                           _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_tree": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
                          _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_tree_e4m3": ([_vp, _vp, _vp, _f32, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
@@ -275,6 +277,24 @@ def decode_tree(q_nope, q_rope, kv_pool, block_table, seq_lens, tree_mask, softm
                           float(softmax_scale), int(num_partitions), _ptr(out), _ptr(lse),
                           _ptr(workspace), workspace.numel(), _stream_handle(stream))
     _check(st, name)
+    return out, lse
+
+
+def decode_varlen(q_nope, q_rope, kv_pool, block_table, seq_lens, q_lens, softmax_scale,
+                  num_partitions=0, out=None, lse=None, workspace=None, stream=None):
+    """mla_decode_varlen: request b verifies q_lens[b] (int32 [B], device) of the Sq
+    query slots; padding slots come back as O = 0, LSE = -inf."""
+    torch = _torch()
+    B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table, seq_lens,
+                                                out, lse, workspace, num_partitions)
+    if q_lens.dtype != torch.int32 or tuple(q_lens.shape) != (B,) or not q_lens.is_cuda:
+        raise ValueError("q_lens must be an int32 [B] device tensor")
+    st = lib().mla_decode_varlen(_ptr(q_nope), _ptr(q_rope), _ptr(kv_pool), kv_pool.shape[0],
+                                 PAGE_SIZE, _ptr(block_table), maxp, _ptr(seq_lens),
+                                 _ptr(q_lens), B, Sq, H, float(softmax_scale),
+                                 int(num_partitions), _ptr(out), _ptr(lse), _ptr(workspace),
+                                 workspace.numel(), _stream_handle(stream))
+    _check(st, "mla_decode_varlen")
     return out, lse
 
 

@@ -152,9 +152,12 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
                   const void* kv_pool, int kv_e4m3, float kv_scale, int64_t num_pages,
                   const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                   const uint64_t* tree_mask, int B, int Sq, int H, float scale, int causal,
-                  float* O, float* lse, bool single_pass, hipStream_t stream) {
+                  float* O, float* lse, bool single_pass, hipStream_t stream,
+                  const int32_t* q_lens = nullptr) {
   SplitArgs a;
   a.tree_mask = tree_mask;
+  a.q_lens = q_lens;
+  a.len_min = q_lens ? 1 : Sq;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
   a.kv_pool = kv_pool;
@@ -229,7 +232,7 @@ int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_p
                 int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
                 float softmax_scale, int causal, int num_partitions, float* O, float* lse,
                 void* workspace, size_t workspace_bytes, void* stream, bool single_pass,
-                const uint64_t* tree_mask = nullptr) {
+                const uint64_t* tree_mask = nullptr, const int32_t* q_lens = nullptr) {
   if (kv_e4m3 && (!(kv_scale > 0.0f) || isinf(kv_scale))) return MLA_ERR_INVALID_ARG;
   Call c;
   int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
@@ -239,7 +242,7 @@ int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_p
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = enqueue_split(c, q_nope, q_rope, kv_pool, kv_e4m3, kv_scale, num_pages, block_table,
                      max_pages_per_seq, seq_lens, tree_mask, B, Sq, H, softmax_scale, causal, O,
-                     lse, single_pass, s);
+                     lse, single_pass, s, q_lens);
   if (st != MLA_OK || single_pass) return st;
   return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
 }
@@ -406,6 +409,17 @@ int mla_decode_tree_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const u
   return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1, num_partitions, O,
                      lse, workspace, workspace_bytes, stream, false, tree_mask);
+}
+
+int mla_decode_varlen(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                      int64_t num_pages, int page_size, const int32_t* block_table,
+                      int max_pages_per_seq, const int32_t* seq_lens, const int32_t* q_lens,
+                      int B, int Sq, int H, float softmax_scale, int num_partitions, float* O,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_lens || (reinterpret_cast<uintptr_t>(q_lens) & 3)) return MLA_ERR_INVALID_ARG;
+  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1, num_partitions, O,
+                     lse, workspace, workspace_bytes, stream, false, nullptr, q_lens);
 }
 
 int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {

@@ -14,6 +14,7 @@ struct SplitArgs {
   const int32_t* block_table;  // [B, max_pages]
   const int32_t* seq_lens;     // [B]
   const uint64_t* tree_mask;   // [B, Sq] draft-tree ancestor bits, or nullptr (a chain)
+  const int32_t* q_lens;       // [B] drafts per request (<= Sq), or nullptr (Sq each)
   float* O;                    // [B, M, 512]
   float* lse;                  // [B, M]  natural log
   float* part_o;               // [slots, slot_rows, 512]  normalised partial outputs
@@ -22,6 +23,7 @@ struct SplitArgs {
   int64_t num_pages;
   int max_pages;
   int B, Sq, H, M;
+  int len_min;                 // smallest valid seq_lens entry: Sq, or 1 with q_lens
   int n_mt;                    // M-tiles per request
   int G;                       // KV partitions
   int slot_rows;               // min(M, M-tile rows)

@@ -649,14 +649,24 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = wave >> 1, c = wave & 1;  // row slice of the M-tile; contraction / column half
   const int M = a.M;
+  // drafts of this request: Sq, or q_lens[b] (query slots past it are padding that
+  // sees nothing, so its rows come out as O = 0, LSE = -inf)
+  int sq = a.Sq;
+  if (a.q_lens) {
+    // one value per request, kept in a scalar register like the other per-piece
+    // bounds (an out-of-range count is reported by the kernel's prologue)
+    const int want = __builtin_amdgcn_readfirstlane(a.q_lens[b]);
+    sq = min(max(want, 1), min(a.Sq, max(L, 1)));
+  }
   const int m_slice = mt * kMTile + p * kRowsPerWave;
   const int m_q = m_slice + (lane & 31);  // the query row this lane scores
-  const bool q_ok = m_q < M;
+  const bool q_ok = m_q < sq * a.H;
   const int t = q_ok ? m_q / a.H : 0;
-  const int n_vis = a.causal ? L - a.Sq + t + 1 : L;
-  // rows the M-tile's last query row sees: blocks past it are skipped by every wave
-  const int m_last = min(M, (mt + 1) * kMTile) - 1;
-  const int n_vis_max = a.causal ? L - a.Sq + m_last / a.H + 1 : L;
+  const int n_vis = !q_ok ? 0 : (a.causal ? L - sq + t + 1 : L);
+  // rows the M-tile's last real query row sees: blocks past it are skipped by every
+  // wave (a tile of padding rows sees none)
+  const int m_last = min(sq * a.H, (mt + 1) * kMTile) - 1;
+  const int n_vis_max = m_last < mt * kMTile ? 0 : (a.causal ? L - sq + m_last / a.H + 1 : L);
   const int nb = max(0, min(2 * (hi - lo), (n_vis_max + kKvBlock - 1) / kKvBlock - 2 * lo));
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query row m_q, for k-step kk the
@@ -693,7 +703,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   uint64_t tm = 0;
   int d_first = 1 << 30;  // no tree: no block holds draft rows
   if (a.tree_mask) {
-    d_first = L - a.Sq;
+    d_first = L - sq;
     if (q_ok) tm = (a.tree_mask[(size_t)b * a.Sq + t] & ((2ull << t) - 1ull)) | (1ull << t);
   }
   auto drow_of = [&](int i) {
@@ -1118,7 +1128,13 @@ splitkv_kernel(SplitArgs a) {
   // first piece starts
   int* prefix = reinterpret_cast<int*>(xbuf);
   int* lens = prefix + kMaxBatch + 1;
-  build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, true, lens);
+  build_page_prefix(a.seq_lens, a.B, a.len_min, a.max_pages, prefix, a.flags, true, lens);
+  if (a.q_lens && threadIdx.x < 64) {  // per-request draft counts outside [1, min(Sq, L_b)]
+    for (int j = threadIdx.x; j < a.B; j += 64) {
+      const int q = a.q_lens[j];
+      if (q < 1 || q > min(a.Sq, lens[j])) atomicOr(a.flags, kFlagBadSeqLen);
+    }
+  }
   const int64_t T = prefix[a.B];
   const int64_t p0 = part_begin(T, a.G, g);
   const int64_t p1 = part_begin(T, a.G, g + 1);
@@ -1136,7 +1152,8 @@ splitkv_kernel(SplitArgs a) {
   // walk the requests the partition touches; a request's page count is recomputed
   // from its clamped length (the same count the prefix was built from)
   for (int b = lo; b < a.B && pb0 < p1; ++b) {
-    const int Lb = b == lo ? L_first : clamp_len(a.seq_lens[b], a.Sq, a.max_pages, a.flags, false);
+    const int Lb = b == lo ? L_first : clamp_len(a.seq_lens[b], a.len_min, a.max_pages, a.flags,
+                                                  false);
     const int pb1 = pb0 + (Lb + kPage - 1) / kPage;
     if (pb1 > pb0) {
       const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);

@@ -24,7 +24,7 @@ def test_library_exports_every_header_function():
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
         "mla_decode_splitkv_e4m3", "mla_decode_tree", "mla_decode_tree_e4m3",
-        "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
+        "mla_decode_varlen", "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
         "mla_status_string"])
     L = mla.lib()
     for n in names:
@@ -155,6 +155,16 @@ def _tree_call(name="mla_decode_tree", **over):
 ])
 def test_tree_entry_points_reject_on_host(name, over, code):
     assert _tree_call(name, **over) == code
+
+
+def test_varlen_rejects_on_host():
+    L = mla.lib()
+    args = [FAKE, FAKE, FAKE, 8, 64, FAKE, 4, FAKE]
+    rest = [1, 4, 16, 0.07, 2, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert L.mla_decode_varlen(*args, None, *rest) == INVALID
+    assert L.mla_decode_varlen(*args, FAKE + 2, *rest) == INVALID
+    assert L.mla_decode_varlen(*args, FAKE, 1, 4, 16, 0.07, 2, FAKE, FAKE, None, 1 << 30,
+                               None) == WORKSPACE
 
 
 def test_tree_e4m3_rejects_bad_scale():
