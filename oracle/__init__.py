@@ -20,4 +20,6 @@ from .mla_oracle import (  # noqa: F401
     mla_attention_tree_loop,
     mla_attention_tree_rows,
     mla_attention_varlen,
+    e4m3_quantize,
+    kv_append,
 )

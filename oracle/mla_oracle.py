@@ -352,6 +352,40 @@ def mla_attention_varlen(q_nope, q_rope, pool, block_table, seq_lens, scale, q_l
     return O, LSE
 
 
+def e4m3_quantize(x) -> np.ndarray:
+    """float32 values -> E4M3 codes: the nearest E4M3 value, ties to the code with an
+    even mantissa, magnitudes past the largest finite value (448) saturated to it.
+
+    Written as a search over the 127 finite non-negative codes (decoded by
+    e4m3_bits_to_f64), not by bit manipulation.  Sign is kept, so -0.0 gives 0x80.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    codes = np.arange(127, dtype=np.uint8)           # 0x00 .. 0x7E (0x7F is NaN)
+    vals = e4m3_bits_to_f64(codes)                    # increasing, 0 .. 448
+    a = np.minimum(np.abs(x), vals[-1])
+    d = np.abs(a[..., None] - vals)                   # distance to every code
+    best = d.min(axis=-1, keepdims=True)
+    tie = d == best                                   # one or two nearest codes
+    even = tie & (codes % 2 == 0)
+    pick = np.where(even.any(axis=-1), even.argmax(axis=-1), tie.argmax(axis=-1))
+    return (codes[pick] | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def kv_append(pool, block_table, seq_lens, kv_new):
+    """The pool after writing each request's new latent rows: kv_new[b, t] (t < Sq)
+    becomes logical row L_b - Sq + t of request b, i.e. the rows the decode then
+    reads as its drafts ("absorb + project" brackets the attention; the new tokens'
+    latents are cached before they are attended to).  Returns a new array."""
+    out = np.array(pool, copy=True)
+    B, Sq = kv_new.shape[:2]
+    for b in range(B):
+        L = int(seq_lens[b])
+        for t in range(Sq):
+            j = L - Sq + t
+            out[block_table[b, j // PAGE_ROWS], j % PAGE_ROWS] = kv_new[b, t]
+    return out
+
+
 def lse_merge(parts):
     """Merge split partials [(O_s, LSE_s), ...] into (O, LSE).
 
