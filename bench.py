@@ -92,6 +92,35 @@ def cpu_baseline(w, budget_s=12.0):
             "seconds_per_step_extrapolated": dt * w.B / done}
 
 
+def measured_peaks(torch, dev):
+    """Achievable peaks on this device, for context beside the spec-sheet ones: a plain
+    2 GiB device-to-device copy (bytes read + written per second) and a 8192^3 bf16
+    matmul through torch (hipBLASLt), each timed with events over back-to-back runs."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    k = 8192
+    x = torch.randn(k, k, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(k, k, device=dev, dtype=torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(x, y), 10)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": round(2 * n / t_copy / 1e9, 1),
+            "mfma_bf16_matmul_TFLOPs": round(2 * k ** 3 / t_mm / 1e12, 1)}
+
+
 def stored_traffic(config, kv):
     """HBM bytes per split-KV launch from profiles/traffic_<config>[_e4m3].json, if
     the counters were taken on the current kernel sources."""
@@ -123,6 +152,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies cycled per step (0 = enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the copy / matmul measurement of achievable peaks")
     ap.add_argument("--no-single-pass", action="store_true",
                     help="skip the one-launch comparison (profiler runs: every split-KV kernel "
                          "launch is then a split pass alone)")
@@ -245,6 +276,29 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # The cache write of a step's new rows (mla_kv_append[_e4m3]), timed back to back
+    # after every decode timing (it rewrites the draft rows of the pools).
+    from mla_latent_kv_16_amd.workloads import f32_to_bf16_bits
+    kv_new = torch.from_numpy(f32_to_bf16_bits(np.random.default_rng(1).standard_normal(
+        (w.B, w.Sq, 576)).astype(np.float32)).view(np.int16)).to(dev)
+    app_ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+    appends = [mla.bound_kv_append(kv_new, p, bt, sl, app_ws, kv_scale) for p in pools]
+    for i in range(3):
+        appends[i % n_copies]()
+    aev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    aev[0].record()
+    for i in range(50):
+        appends[i % n_copies]()
+    aev[1].record()
+    torch.cuda.synchronize()
+    append_us = aev[0].elapsed_time(aev[1]) / 50 * 1e3
+    if mla.read_error_flags(app_ws):
+        raise SystemExit("kv append reported a data fault flag")
+    append_bytes = w.B * w.Sq * 576 * (2 + w.row_bytes // 576)
+
+    peaks = None if args.no_measured_peaks else measured_peaks(torch, dev)
+
     value = work["kv_bytes"] / (ms_step * 1e-3) / 1e9
     # the dominant kernel's average launch duration: per-launch events on its stream
     hbm_achieved = work["bytes"] / (split_avg * 1e-3) / 1e9
@@ -261,6 +315,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(hbm_achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic}
+    if peaks:
+        key = "mfma_bf16_matmul_TFLOPs" if mfma_bound else "hbm_copy_GBps"
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / peaks[key], 4)
     log(f"step {ms_step * 1e3:.1f} us (split pass {split_avg * 1e3:.1f} us with per-launch events, "
         f"p10 {np.percentile(split_ms, 10) * 1e3:.1f} p90 {np.percentile(split_ms, 90) * 1e3:.1f}; "
         f"{split_b2b * 1e3:.1f} us back to back); {value:.0f} GB/s of KV; split kernel "
@@ -304,7 +361,10 @@ def main():
         "single_pass_us_per_step": None if single_pass_us is None else round(single_pass_us, 2),
         "split_pass_hbm_frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
         "split_pass_mfma_frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kv_append_us": round(append_us, 2),
+        "kv_append_GBps": round(append_bytes / (append_us * 1e-6) / 1e9, 2),
         "roofline": roof,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

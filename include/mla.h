@@ -260,6 +260,32 @@ int mla_decode_varlen(const uint16_t* q_nope, const uint16_t* q_rope, const uint
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Writes the new tokens' latent rows into the pool: kv_new[b, t] becomes logical
+ * row L_b - Sq + t of request b (the rows mla_decode then verifies as its drafts),
+ * found through the block table.  The rows around the attention are the pages'
+ * "absorb + project" brackets (TokenSpeed review page, Attack 1); this is the cache
+ * write that comes first.  The E4M3 variant stores the code of
+ * value * fp32(1 / kv_scale): the nearest E4M3 value, ties to the even code,
+ * saturated at +-448 (non-finite values saturate too).
+ *
+ *   kv_new      bf16 [B, Sq, 576], 16-byte aligned device memory
+ *   kv_pool     the pool (bf16 or E4M3 codes, [num_pages, 64, 576], 16-byte aligned)
+ *   seq_lens    visible rows per request INCLUDING the Sq new ones (as for the decode)
+ *   workspace   at least its 256-byte error-flag header (zeroed before first use)
+ *
+ * A request whose length is outside [Sq, 64 * max_pages_per_seq], or a row whose
+ * page id is outside [0, num_pages), is not written and raises the matching
+ * MLA_FLAG_*.  Rows written by one call must not share a pool row.
+ */
+int mla_kv_append(const uint16_t* kv_new, uint16_t* kv_pool, int64_t num_pages, int page_size,
+                  const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+                  int B, int Sq, void* workspace, size_t workspace_bytes, void* stream);
+int mla_kv_append_e4m3(const uint16_t* kv_new, uint8_t* kv_pool, float kv_scale,
+                       int64_t num_pages, int page_size, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Waits for `stream`, then copies the workspace header's error flags
  * (MLA_FLAG_*) to *flags and clears them.  Reading forces a synchronisation, so
  * callers use it in checked runs and tests, not on the hot path.

@@ -7,6 +7,7 @@ Importing this package loads nothing; the library is opened on first use.
 """
 from ._binding import (  # noqa: F401
     BoundDecode,
+    bound_kv_append,
     MLAError,
     LIB_PATH,
     auto_partitions,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     decode_tree,
     decode_varlen,
     header_functions,
+    kv_append,
     lib,
     new_workspace,
     prefill_with_prefix,

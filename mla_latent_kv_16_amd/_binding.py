@@ -47,6 +47,9 @@ _SIGNATURES = {
     "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
     "mla_decode_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_single_pass": (_COMPUTE_ARGS, _i32),
+    "mla_kv_append": ([_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp], _i32),
+    "mla_kv_append_e4m3": ([_vp, _vp, _f32, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _sz,
+                            _vp], _i32),
     "mla_decode_varlen": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
                            _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_tree": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
@@ -296,6 +299,44 @@ def decode_varlen(q_nope, q_rope, kv_pool, block_table, seq_lens, q_lens, softma
                                  workspace.numel(), _stream_handle(stream))
     _check(st, "mla_decode_varlen")
     return out, lse
+
+
+def kv_append(kv_new, kv_pool, block_table, seq_lens, workspace, kv_scale=None, stream=None):
+    """mla_kv_append (bf16 pool) or mla_kv_append_e4m3 (uint8 pool, with kv_scale):
+    kv_new bf16 [B, Sq, 576] becomes each request's last Sq logical rows."""
+    bound_kv_append(kv_new, kv_pool, block_table, seq_lens, workspace, kv_scale, stream)()
+    return kv_pool
+
+
+def bound_kv_append(kv_new, kv_pool, block_table, seq_lens, workspace, kv_scale=None,
+                    stream=None):
+    """kv_append with its arguments checked and marshalled once: returns a callable
+    that makes the single foreign call (for loops that repeat the same write)."""
+    torch = _torch()
+    e4m3 = kv_scale is not None
+    if kv_new.dim() != 3 or kv_new.shape[2] != 576 or kv_new.dtype not in (torch.bfloat16,
+                                                                              torch.int16):
+        raise ValueError("kv_new must be bf16 [B, Sq, 576]")
+    want = torch.uint8 if e4m3 else (torch.bfloat16, torch.int16)
+    if (kv_pool.dtype != want) if e4m3 else (kv_pool.dtype not in want):
+        raise ValueError("kv_pool dtype does not match the pool format")
+    for name, t in (("kv_new", kv_new), ("kv_pool", kv_pool), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("workspace", workspace)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, Sq = kv_new.shape[:2]
+    L = lib()
+    pool = (_ptr(kv_pool), float(kv_scale)) if e4m3 else (_ptr(kv_pool),)
+    name = "mla_kv_append_e4m3" if e4m3 else "mla_kv_append"
+    fn = getattr(L, name)
+    args = (_ptr(kv_new), *pool, kv_pool.shape[0], PAGE_SIZE, _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), B, Sq, _ptr(workspace), workspace.numel(),
+            _stream_handle(stream))
+    keep = (kv_new, kv_pool, block_table, seq_lens, workspace)
+
+    def call(_keep=keep):
+        _check(fn(*args), name)
+    return call
 
 
 def decode_splitkv(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,

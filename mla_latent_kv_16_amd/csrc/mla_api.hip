@@ -422,6 +422,51 @@ int mla_decode_varlen(const uint16_t* q_nope, const uint16_t* q_rope, const uint
                      lse, workspace, workspace_bytes, stream, false, nullptr, q_lens);
 }
 
+static int append_call(const uint16_t* kv_new, void* kv_pool, int e4m3, float kv_scale,
+                       int64_t num_pages, int page_size, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv_new || !kv_pool || !block_table || !seq_lens) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(kv_new) || !aligned16(kv_pool)) return MLA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3) || (reinterpret_cast<uintptr_t>(seq_lens) & 3))
+    return MLA_ERR_INVALID_ARG;
+  if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (num_pages < 1 || B < 1 || Sq < 1 || max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (e4m3 && (!(kv_scale > 0.0f) || isinf(kv_scale))) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)B * Sq > (1 << 24) || (int64_t)max_pages_per_seq * kPage > 0x3fffffff)
+    return MLA_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < (size_t)kHeaderBytes)
+    return MLA_ERR_WORKSPACE;
+  AppendArgs a;
+  a.kv_new = kv_new;
+  a.kv_pool = kv_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.flags = static_cast<uint32_t*>(workspace);
+  a.num_pages = num_pages;
+  a.max_pages = max_pages_per_seq;
+  a.B = B;
+  a.Sq = Sq;
+  a.e4m3 = e4m3;
+  a.inv_scale = e4m3 ? 1.0f / kv_scale : 1.0f;
+  return launch_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_kv_append(const uint16_t* kv_new, uint16_t* kv_pool, int64_t num_pages, int page_size,
+                  const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+                  int B, int Sq, void* workspace, size_t workspace_bytes, void* stream) {
+  return append_call(kv_new, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, workspace, workspace_bytes, stream);
+}
+
+int mla_kv_append_e4m3(const uint16_t* kv_new, uint8_t* kv_pool, float kv_scale,
+                       int64_t num_pages, int page_size, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return append_call(kv_new, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, workspace, workspace_bytes, stream);
+}
+
 int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {
   if (!workspace || !flags) return MLA_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -55,7 +55,23 @@ struct CombineArgs {
   int n_mt, G, MT, slot_rows;
 };
 
+// Writing new latent rows into the pool (bf16 copy, or E4M3 codes of value * inv_scale).
+constexpr int kAppendThreads = 256;
+struct AppendArgs {
+  const uint16_t* kv_new;      // [B, Sq, 576] bf16
+  void* kv_pool;               // [num_pages, 64, 576] bf16, or E4M3 codes when e4m3
+  const int32_t* block_table;  // [B, max_pages]
+  const int32_t* seq_lens;     // [B]
+  uint32_t* flags;             // workspace header word
+  int64_t num_pages;
+  int max_pages;
+  int B, Sq;
+  int e4m3;
+  float inv_scale;             // fp32(1 / kv_scale) for E4M3 pools
+};
+
 // Launch helpers (defined next to the kernels).
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

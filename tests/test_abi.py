@@ -24,7 +24,7 @@ def test_library_exports_every_header_function():
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
         "mla_decode_splitkv_e4m3", "mla_decode_tree", "mla_decode_tree_e4m3",
-        "mla_decode_varlen", "mla_decode_workspace_size", "mla_prefill_with_prefix", "mla_read_error_flags",
+        "mla_decode_varlen", "mla_decode_workspace_size", "mla_kv_append", "mla_kv_append_e4m3", "mla_prefill_with_prefix", "mla_read_error_flags",
         "mla_status_string"])
     L = mla.lib()
     for n in names:
@@ -165,6 +165,23 @@ def test_varlen_rejects_on_host():
     assert L.mla_decode_varlen(*args, FAKE + 2, *rest) == INVALID
     assert L.mla_decode_varlen(*args, FAKE, 1, 4, 16, 0.07, 2, FAKE, FAKE, None, 1 << 30,
                                None) == WORKSPACE
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(new=None), INVALID), (dict(pool=None), INVALID), (dict(new=FAKE + 8), INVALID),
+    (dict(pool=FAKE + 2), INVALID), (dict(bt=FAKE + 2), INVALID), (dict(page=32), UNSUPPORTED),
+    (dict(B=0), INVALID), (dict(Sq=0), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=128), WORKSPACE), (dict(scale=0.0), INVALID), (dict(scale=math.inf), INVALID),
+])
+def test_kv_append_rejects_on_host(over, code):
+    a = dict(new=FAKE, pool=FAKE, bt=FAKE, sl=FAKE, page=64, B=2, Sq=4, ws=FAKE, ws_bytes=256,
+             scale=0.015625)
+    a.update(over)
+    L = mla.lib()
+    common = (a["page"], a["bt"], 8, a["sl"], a["B"], a["Sq"], a["ws"], a["ws_bytes"], None)
+    if "scale" not in over:
+        assert L.mla_kv_append(a["new"], a["pool"], 16, *common) == code
+    assert L.mla_kv_append_e4m3(a["new"], a["pool"], a["scale"], 16, *common) == code
 
 
 def test_tree_e4m3_rejects_bad_scale():
