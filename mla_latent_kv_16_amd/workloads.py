@@ -165,7 +165,7 @@ class Workload:
 
     @property
     def row_bytes(self) -> int:
-        return D_ROW * (1 if self.kv_format == "e4m3" else 2)
+        return self.kv_pool.shape[2] * (1 if self.kv_format == "e4m3" else 2)
 
     def kv_bytes(self) -> int:
         """Latent bytes a step must read: every visible row once (576 bf16 or E4M3)."""
@@ -187,12 +187,14 @@ def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] 
                   q_sigma: Optional[float] = None, kv_sigma: Optional[float] = None,
                   poison: bool = True, pool_factor: int = 2,
                   scale: Optional[float] = None, kv_format: str = "bf16",
-                  kv_scale: Optional[float] = None) -> Workload:
+                  kv_scale: Optional[float] = None, rope: bool = True) -> Workload:
     """Build one seeded workload.  Any keyword overrides the named spec.  With
     kv_format="e4m3" the latent rows are the same draws stored as E4M3 codes of
     value / kv_scale."""
     if kv_format not in ("bf16", "e4m3"):
         raise ValueError(kv_format)
+    # rope=False: NoPE-MLA, pool rows are the 512-wide latent alone and q_rope is empty
+    width = D_ROW if rope else D_C
     kvs = float(DEFAULT_KV_SCALE if kv_scale is None else kv_scale)
     spec = WORKLOADS[spec_or_name] if isinstance(spec_or_name, str) else spec_or_name
     over = {k: v for k, v in dict(seed=seed, B=B, Sq=Sq, H=H, lens=lens, causal=causal,
@@ -218,13 +220,13 @@ def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] 
 
     if kv_format == "e4m3":
         fill = E4M3_NAN if poison else np.uint8(0)
-        pool = np.full((pool_pages, PAGE, D_ROW), fill, dtype=np.uint8)
+        pool = np.full((pool_pages, PAGE, width), fill, dtype=np.uint8)
     else:
         fill = BF16_NAN if poison else np.uint16(0)
-        pool = np.full((pool_pages, PAGE, D_ROW), fill, dtype=np.uint16)
+        pool = np.full((pool_pages, PAGE, width), fill, dtype=np.uint16)
     for b in range(Bn):
         Lb = int(L[b])
-        draws = rng.standard_normal((Lb, D_ROW), dtype=np.float32) * np.float32(spec.kv_sigma)
+        draws = rng.standard_normal((Lb, width), dtype=np.float32) * np.float32(spec.kv_sigma)
         if kv_format == "e4m3":
             rows = f32_to_e4m3_bits(draws / np.float32(kvs))
         else:
@@ -233,7 +235,7 @@ def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] 
         n = int(pages_per[b])
         full = Lb // PAGE
         if full:
-            pool[block_table[b, :full]] = rows[:full * PAGE].reshape(full, PAGE, D_ROW)
+            pool[block_table[b, :full]] = rows[:full * PAGE].reshape(full, PAGE, width)
         if n > full:
             tail = Lb - full * PAGE
             pool[block_table[b, full], :tail] = rows[full * PAGE:]
@@ -241,7 +243,8 @@ def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] 
 
     q_nope = f32_to_bf16_bits(rng.standard_normal((Bn, Sqn, Hn, D_C), dtype=np.float32)
                               * np.float32(spec.q_sigma))
-    q_rope = f32_to_bf16_bits(rng.standard_normal((Bn, Sqn, Hn, D_R), dtype=np.float32)
+    q_rope = f32_to_bf16_bits(rng.standard_normal((Bn, Sqn, Hn, D_R if rope else 0),
+                                                  dtype=np.float32)
                               * np.float32(spec.q_sigma))
     sc = DEFAULT_SCALE if scale is None else np.float32(scale)
     return Workload(spec, q_nope, q_rope, pool, block_table, L.astype(np.int32), sc,

@@ -21,5 +21,6 @@ from .mla_oracle import (  # noqa: F401
     mla_attention_tree_rows,
     mla_attention_varlen,
     e4m3_quantize,
+    mla_attention_nope,
     kv_append,
 )

@@ -386,6 +386,36 @@ def kv_append(pool, block_table, seq_lens, kv_new):
     return out
 
 
+def mla_attention_nope(q_nope, pool, block_table, seq_lens, scale, causal=True, b_m=None):
+    """NoPE-MLA: the cached row is the 512-wide latent alone (no decoupled RoPE key;
+    "Faster kernels, slower engine", "Two stacks, one inverted flag": Kimi-K3's MLA
+    layers are NoPE-MLA).  Scores are scale * q_nope . c_kv and the values are c_kv.
+    pool [P, 64, 512].  Returns fp64 (O [B,Sq,H,512], LSE [B,Sq,H]); with
+    b_m = (b, m_list), only those folded rows of request b: (O [n,512], LSE [n])."""
+    B, Sq, H = q_nope.shape[:3]
+    M = Sq * H
+
+    def one(b, m_idx):
+        L = int(seq_lens[b])
+        rows = gather_latent_rows(pool, block_table, b, L)          # [L, 512]
+        Q = _f64(q_nope[b]).reshape(M, NOPE)[m_idx]
+        S = (Q @ rows.T) * float(scale)
+        t = m_idx // H
+        n_vis = (L - Sq + t + 1) if causal else np.full_like(t, L)
+        S = np.where(np.arange(L)[None, :] < n_vis[:, None], S, -np.inf)
+        mx = S.max(axis=1, keepdims=True)
+        lse = mx[:, 0] + np.log(np.exp(S - mx).sum(axis=1))
+        return np.exp(S - lse[:, None]) @ rows, lse
+
+    if b_m is not None:
+        return one(b_m[0], np.asarray(b_m[1], dtype=np.int64))
+    O = np.zeros((B, M, NOPE))
+    LSE = np.zeros((B, M))
+    for b in range(B):
+        O[b], LSE[b] = one(b, np.arange(M))
+    return O.reshape(B, Sq, H, NOPE), LSE.reshape(B, Sq, H)
+
+
 def lse_merge(parts):
     """Merge split partials [(O_s, LSE_s), ...] into (O, LSE).
 
