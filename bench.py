@@ -53,7 +53,7 @@ def algorithmic_work(w):
     M = w.Sq * w.H
     pages = int(((L + 63) // 64).sum())
     kv = w.kv_bytes()
-    q = w.B * M * 1152
+    q = w.B * M * (512 + w.q_rope.shape[3]) * 2
     out = w.B * M * (512 * 4 + 4)
     bt = pages * 4
     t = np.arange(w.Sq, dtype=np.int64)
@@ -61,14 +61,14 @@ def algorithmic_work(w):
         n_vis = (L[:, None] - w.Sq + t[None, :] + 1).sum()
     else:
         n_vis = L.sum() * w.Sq
-    flops = int(n_vis) * w.H * 2 * (576 + 512)
+    flops = int(n_vis) * w.H * 2 * (w.kv_pool.shape[2] + 512)
     return dict(kv_bytes=kv, bytes=kv + q + out + bt, flops=flops, pages=pages)
 
 
 def cpu_baseline(w, budget_s=12.0):
     """fp64 oracle on whole requests (cycling through the batch) until ~budget_s has
     passed; KV bytes of the requests done over the wall time, in GB/s."""
-    from oracle import E4M3Pool, mla_attention_folded
+    from oracle import E4M3Pool, mla_attention_folded, mla_attention_nope
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -79,8 +79,12 @@ def cpu_baseline(w, budget_s=12.0):
     while True:
         b = done % w.B
         sl = slice(b, b + 1)
-        mla_attention_folded(w.q_nope[sl], w.q_rope[sl], pool, w.block_table[sl],
-                             w.seq_lens[sl], w.scale, w.causal)
+        if w.kv_pool.shape[2] == 512:  # NoPE rows
+            mla_attention_nope(w.q_nope[sl], pool, w.block_table[sl], w.seq_lens[sl], w.scale,
+                               w.causal)
+        else:
+            mla_attention_folded(w.q_nope[sl], w.q_rope[sl], pool, w.block_table[sl],
+                                 w.seq_lens[sl], w.scale, w.causal)
         done += 1
         kv += int(w.seq_lens[b]) * w.row_bytes
         if time.perf_counter() - t0 > budget_s:
@@ -148,6 +152,8 @@ def main():
                     help="tiny | spec4 | spec8 | spec16 | sweep | prefill")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "e4m3"],
                     help="latent pool format: bf16, or E4M3 codes with a per-tensor scale")
+    ap.add_argument("--nope", action="store_true",
+                    help="NoPE-MLA rows (the 512-wide latent alone, no RoPE part; bf16)")
     ap.add_argument("--partitions", type=int, default=0, help="0 = library default")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies cycled per step (0 = enough to exceed 2x MALL)")
@@ -176,7 +182,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    w = make_workload(args.config, kv_format=args.kv)
+    if args.nope and args.kv != "bf16":
+        raise SystemExit("--nope pools are bf16")
+    w = make_workload(args.config, kv_format=args.kv, rope=not args.nope)
     work = algorithmic_work(w)
     log(f"{args.config} ({args.kv} pool): B={w.B} Sq={w.Sq} H={w.H} pages={work['pages']} "
         f"kv={work['kv_bytes'] / 1e6:.1f} MB, generated in {time.perf_counter() - t_gen:.1f}s")
@@ -203,7 +211,7 @@ def main():
     log(f"partitions={G} pool copies={n_copies} ({pool_bytes / 1e9:.2f} GB each)")
 
     calls = [mla.BoundDecode(q_nope, q_rope, pool, bt, sl, scale, w.causal, G, O, lse, ws,
-                             kv_scale=kv_scale) for pool in pools]
+                             kv_scale=kv_scale, nope=args.nope) for pool in pools]
 
     def step(i, ev=None):
         c = calls[i % n_copies]
@@ -257,7 +265,7 @@ def main():
 
     # The same steps in one launch each (mla_decode_single_pass), for comparison.
     single_pass_us = None
-    if G > 1 and not args.no_single_pass:
+    if G > 1 and not args.no_single_pass and not args.nope:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -277,25 +285,28 @@ def main():
         del src, dst
 
     # The cache write of a step's new rows (mla_kv_append[_e4m3]), timed back to back
-    # after every decode timing (it rewrites the draft rows of the pools).
-    from mla_latent_kv_16_amd.workloads import f32_to_bf16_bits
-    kv_new = torch.from_numpy(f32_to_bf16_bits(np.random.default_rng(1).standard_normal(
-        (w.B, w.Sq, 576)).astype(np.float32)).view(np.int16)).to(dev)
-    app_ws = torch.zeros(256, dtype=torch.uint8, device=dev)
-    appends = [mla.bound_kv_append(kv_new, p, bt, sl, app_ws, kv_scale) for p in pools]
-    for i in range(3):
-        appends[i % n_copies]()
-    aev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    torch.cuda.synchronize()
-    aev[0].record()
-    for i in range(50):
-        appends[i % n_copies]()
-    aev[1].record()
-    torch.cuda.synchronize()
-    append_us = aev[0].elapsed_time(aev[1]) / 50 * 1e3
-    if mla.read_error_flags(app_ws):
-        raise SystemExit("kv append reported a data fault flag")
-    append_bytes = w.B * w.Sq * 576 * (2 + w.row_bytes // 576)
+    # after every decode timing (it rewrites the draft rows of the pools); the write
+    # takes 576-wide rows, so NoPE pools skip it.
+    append_us = append_bytes = None
+    if not args.nope:
+        from mla_latent_kv_16_amd.workloads import f32_to_bf16_bits
+        kv_new = torch.from_numpy(f32_to_bf16_bits(np.random.default_rng(1).standard_normal(
+            (w.B, w.Sq, 576)).astype(np.float32)).view(np.int16)).to(dev)
+        app_ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+        appends = [mla.bound_kv_append(kv_new, p, bt, sl, app_ws, kv_scale) for p in pools]
+        for i in range(3):
+            appends[i % n_copies]()
+        aev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        torch.cuda.synchronize()
+        aev[0].record()
+        for i in range(50):
+            appends[i % n_copies]()
+        aev[1].record()
+        torch.cuda.synchronize()
+        append_us = aev[0].elapsed_time(aev[1]) / 50 * 1e3
+        if mla.read_error_flags(app_ws):
+            raise SystemExit("kv append reported a data fault flag")
+        append_bytes = w.B * w.Sq * 576 * (2 + w.row_bytes // 576)
 
     peaks = None if args.no_measured_peaks else measured_peaks(torch, dev)
 
@@ -349,8 +360,9 @@ def main():
         "config": {"workload": args.config, "B": w.B, "Sq": w.Sq, "H": w.H,
                    "context": [int(w.seq_lens.min()), int(w.seq_lens.max())],
                    "page_size": 64,
-                   "latent": "512+64 " + ("e4m3, per-tensor scale" if args.kv == "e4m3"
-                                          else "bf16"),
+                   "latent": ("512 bf16 (NoPE)" if args.nope else
+                              "512+64 " + ("e4m3, per-tensor scale" if args.kv == "e4m3"
+                                           else "bf16")),
                    "partitions": G,
                    "kv_bytes": work["kv_bytes"], "tflops_per_step": work["flops"] / 1e12},
         "kv_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
@@ -361,8 +373,9 @@ def main():
         "single_pass_us_per_step": None if single_pass_us is None else round(single_pass_us, 2),
         "split_pass_hbm_frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
         "split_pass_mfma_frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-        "kv_append_us": round(append_us, 2),
-        "kv_append_GBps": round(append_bytes / (append_us * 1e-6) / 1e9, 2),
+        "kv_append_us": None if append_us is None else round(append_us, 2),
+        "kv_append_GBps": (None if append_us is None
+                           else round(append_bytes / (append_us * 1e-6) / 1e9, 2)),
         "roofline": roof,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,

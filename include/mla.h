@@ -241,6 +241,29 @@ int mla_decode_tree_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const u
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * NoPE-MLA decode: the cached row is the 512-wide latent alone, with no decoupled
+ * RoPE key ("Faster kernels, slower engine", "Two stacks, one inverted flag": the
+ * MI355X runs there serve Kimi-K3, whose MLA layers are NoPE-MLA).  Scores are
+ * softmax_scale * q_nope . c_kv; values are c_kv.  There is no q_rope argument.
+ *
+ *   kv_pool  bf16 [num_pages, 64, 512], 16-byte aligned
+ *
+ * Every other argument, the workspace, the outputs and the combine pass are as for
+ * mla_decode; mla_decode_splitkv_nope is its split-KV pass alone (then
+ * mla_decode_combine), as mla_decode_splitkv is for mla_decode.
+ */
+int mla_decode_nope(const uint16_t* q_nope, const uint16_t* kv_pool, int64_t num_pages,
+                    int page_size, const int32_t* block_table, int max_pages_per_seq,
+                    const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                    int causal, int num_partitions, float* O, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
+int mla_decode_splitkv_nope(const uint16_t* q_nope, const uint16_t* kv_pool, int64_t num_pages,
+                            int page_size, const int32_t* block_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                            int causal, int num_partitions, float* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode with a per-request number of drafts (atlas §16 Speculative decoding: the
  * number of candidates verified per request varies).  Request b verifies
  * q_lens[b] drafts, 1 <= q_lens[b] <= min(Sq, L_b), held in its first q_lens[b]

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     decode,
     decode_combine,
     decode_e4m3,
+    decode_nope,
     decode_single_pass,
     decode_single_pass_e4m3,
     decode_splitkv,

@@ -50,6 +50,10 @@ _SIGNATURES = {
     "mla_kv_append": ([_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp], _i32),
     "mla_kv_append_e4m3": ([_vp, _vp, _f32, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _sz,
                             _vp], _i32),
+    "mla_decode_nope": ([_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32,
+                         _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "mla_decode_splitkv_nope": ([_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                                 _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_varlen": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
                            _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_tree": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
@@ -154,7 +158,9 @@ def new_workspace(B, Sq, H, max_pages_per_seq, num_partitions=0, device=None):
 
 
 def _prep(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace, num_partitions,
-          e4m3=False):
+          e4m3=False, nope=False):
+    """Checks shapes, dtypes and placement; allocates missing outputs and workspace.
+    nope: 512-wide pool rows and no q_rope (q_rope is then ignored)."""
     torch = _torch()
     bf = (torch.bfloat16, torch.int16)
     if q_nope.dim() != 4:
@@ -163,9 +169,11 @@ def _prep(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace, n
     if D != NOPE_DIM:
         raise ValueError("q_nope last dim must be 512")
     _expect(q_nope, "q_nope", bf)
-    _expect(q_rope, "q_rope", bf, (B, Sq, H, ROPE_DIM))
-    if kv_pool.dim() != 3 or kv_pool.shape[1] != PAGE_SIZE or kv_pool.shape[2] != NOPE_DIM + ROPE_DIM:
-        raise ValueError("kv_pool must be [num_pages, 64, 576]")
+    if not nope:
+        _expect(q_rope, "q_rope", bf, (B, Sq, H, ROPE_DIM))
+    width = NOPE_DIM if nope else NOPE_DIM + ROPE_DIM
+    if kv_pool.dim() != 3 or kv_pool.shape[1] != PAGE_SIZE or kv_pool.shape[2] != width:
+        raise ValueError(f"kv_pool must be [num_pages, 64, {width}]")
     _expect(kv_pool, "kv_pool", (torch.uint8,) if e4m3 else bf)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_pages_per_seq]")
@@ -283,6 +291,20 @@ def decode_tree(q_nope, q_rope, kv_pool, block_table, seq_lens, tree_mask, softm
     return out, lse
 
 
+def decode_nope(q_nope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
+                num_partitions=0, out=None, lse=None, workspace=None, stream=None):
+    """mla_decode_nope: NoPE-MLA decode, kv_pool bf16 [P, 64, 512], no q_rope."""
+    B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, None, kv_pool, block_table, seq_lens,
+                                                out, lse, workspace, num_partitions, nope=True)
+    st = lib().mla_decode_nope(_ptr(q_nope), _ptr(kv_pool), kv_pool.shape[0], PAGE_SIZE,
+                               _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H,
+                               float(softmax_scale), 1 if causal else 0, int(num_partitions),
+                               _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                               _stream_handle(stream))
+    _check(st, "mla_decode_nope")
+    return out, lse
+
+
 def decode_varlen(q_nope, q_rope, kv_pool, block_table, seq_lens, q_lens, softmax_scale,
                   num_partitions=0, out=None, lse=None, workspace=None, stream=None):
     """mla_decode_varlen: request b verifies q_lens[b] (int32 [B], device) of the Sq
@@ -317,6 +339,8 @@ def bound_kv_append(kv_new, kv_pool, block_table, seq_lens, workspace, kv_scale=
     if kv_new.dim() != 3 or kv_new.shape[2] != 576 or kv_new.dtype not in (torch.bfloat16,
                                                                               torch.int16):
         raise ValueError("kv_new must be bf16 [B, Sq, 576]")
+    if kv_pool.dim() != 3 or tuple(kv_pool.shape[1:]) != (PAGE_SIZE, 576):
+        raise ValueError("kv_pool must be [num_pages, 64, 576] (rows of the width kv_new has)")
     want = torch.uint8 if e4m3 else (torch.bfloat16, torch.int16)
     if (kv_pool.dtype != want) if e4m3 else (kv_pool.dtype not in want):
         raise ValueError("kv_pool dtype does not match the pool format")
@@ -383,23 +407,27 @@ class BoundDecode:
 
     def __init__(self, q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
                  num_partitions=0, out=None, lse=None, workspace=None, stream=None,
-                 kv_scale=None):
+                 kv_scale=None, nope=False):
         e4m3 = kv_scale is not None  # an E4M3 pool comes with its scale
         B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table,
                                                     seq_lens, out, lse, workspace, num_partitions,
-                                                    e4m3=e4m3)
+                                                    e4m3=e4m3, nope=nope)
         self.tensors = (q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse, workspace)
         self.out, self.lse, self.workspace = out, lse, workspace
         self.num_partitions = int(num_partitions) or auto_partitions(B, Sq, H, maxp)
         pool_args = ((_ptr(kv_pool), float(kv_scale)) if e4m3 else (_ptr(kv_pool),))
-        self._args = (_ptr(q_nope), _ptr(q_rope), *pool_args, kv_pool.shape[0], PAGE_SIZE,
+        q_args = (_ptr(q_nope),) if nope else (_ptr(q_nope), _ptr(q_rope))
+        self._args = (*q_args, *pool_args, kv_pool.shape[0], PAGE_SIZE,
                       _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H, float(softmax_scale),
                       1 if causal else 0, self.num_partitions, _ptr(out), _ptr(lse),
                       _ptr(workspace), workspace.numel(), _stream_handle(stream))
         self._cargs = (_ptr(seq_lens), maxp, B, Sq, H, self.num_partitions, _ptr(out), _ptr(lse),
                        _ptr(workspace), workspace.numel(), _stream_handle(stream))
         L = lib()
-        if e4m3:
+        if nope:
+            self._decode, self._split = L.mla_decode_nope, L.mla_decode_splitkv_nope
+            self._single = None
+        elif e4m3:
             self._decode, self._split = L.mla_decode_e4m3, L.mla_decode_splitkv_e4m3
             self._single = L.mla_decode_single_pass_e4m3
         else:
@@ -411,6 +439,8 @@ class BoundDecode:
         _check(self._decode(*self._args), "mla_decode")
 
     def single_pass(self):
+        if self._single is None:
+            raise ValueError("no single-pass entry point for NoPE pools")
         _check(self._single(*self._args), "mla_decode_single_pass")
 
     def splitkv(self):

@@ -12,6 +12,8 @@ namespace {
 using namespace mla;
 
 constexpr int kMaxDevices = 64;
+// pool row formats
+constexpr int kFormatBf16 = 0, kFormatE4m3 = 1, kFormatNope = 2;
 int g_cu_count[kMaxDevices];
 std::once_flag g_cu_once[kMaxDevices];
 
@@ -108,7 +110,8 @@ Layout carve(void* ws, const Geometry& g, int B, int G) {
   l.arrive = reinterpret_cast<uint32_t*>(base + kHeaderBytes);
   l.done = l.arrive + (size_t)B * g.n_mt;
   l.part_o = reinterpret_cast<float*>(base + kHeaderBytes + cnt);
-  l.part_lse = reinterpret_cast<float*>(base + kHeaderBytes + cnt + slots * g.slot_rows * kNope * 4);
+  l.part_lse =
+      reinterpret_cast<float*>(base + kHeaderBytes + cnt + slots * g.slot_rows * kNope * 4);
   return l;
 }
 
@@ -130,7 +133,8 @@ int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool,
     return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_pool) || !aligned16(O))
     return MLA_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(block_table) & 3) || (reinterpret_cast<uintptr_t>(seq_lens) & 3) ||
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3) ||
       (reinterpret_cast<uintptr_t>(lse) & 3))
     return MLA_ERR_INVALID_ARG;
   if (page_size != kPage) return MLA_ERR_UNSUPPORTED;
@@ -149,7 +153,7 @@ int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool,
 }
 
 int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
-                  const void* kv_pool, int kv_e4m3, float kv_scale, int64_t num_pages,
+                  const void* kv_pool, int kv_format, float kv_scale, int64_t num_pages,
                   const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                   const uint64_t* tree_mask, int B, int Sq, int H, float scale, int causal,
                   float* O, float* lse, bool single_pass, hipStream_t stream,
@@ -178,7 +182,8 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
   a.G = c.G;
   a.slot_rows = c.geo.slot_rows;
   a.causal = causal;
-  a.kv_e4m3 = kv_e4m3;
+  a.kv_e4m3 = kv_format == kFormatE4m3;
+  a.kv_nope = kv_format == kFormatNope;
   a.kv_scale = kv_scale;
   a.scale_log2 = scale * kv_scale * 1.4426950408889634f;
   a.n_split = c.G * c.geo.n_mt;
@@ -227,20 +232,21 @@ int enqueue_combine(const Call& c, const int32_t* seq_lens, int max_pages, int B
 
 // One decode: the split-KV pass, then the separate merge kernel, or both in one
 // launch (single_pass).
-int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool, int kv_e4m3,
+int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool, int kv_format,
                 float kv_scale, int64_t num_pages, int page_size, const int32_t* block_table,
                 int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
                 float softmax_scale, int causal, int num_partitions, float* O, float* lse,
                 void* workspace, size_t workspace_bytes, void* stream, bool single_pass,
                 const uint64_t* tree_mask = nullptr, const int32_t* q_lens = nullptr) {
-  if (kv_e4m3 && (!(kv_scale > 0.0f) || isinf(kv_scale))) return MLA_ERR_INVALID_ARG;
+  if (kv_format == kFormatE4m3 && (!(kv_scale > 0.0f) || isinf(kv_scale)))
+    return MLA_ERR_INVALID_ARG;
   Call c;
   int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = enqueue_split(c, q_nope, q_rope, kv_pool, kv_e4m3, kv_scale, num_pages, block_table,
+  st = enqueue_split(c, q_nope, q_rope, kv_pool, kv_format, kv_scale, num_pages, block_table,
                      max_pages_per_seq, seq_lens, tree_mask, B, Sq, H, softmax_scale, causal, O,
                      lse, single_pass, s, q_lens);
   if (st != MLA_OK || single_pass) return st;
@@ -293,7 +299,7 @@ int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uin
                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
-  return enqueue_split(c, q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, block_table,
+  return enqueue_split(c, q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, block_table,
                        max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
                        lse, false, static_cast<hipStream_t>(stream));
 }
@@ -320,7 +326,7 @@ int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* k
                int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
                float softmax_scale, int causal, int num_partitions, float* O, float* lse,
                void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+  return decode_call(q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
                      num_partitions, O, lse, workspace, workspace_bytes, stream, false);
 }
@@ -331,7 +337,7 @@ int mla_decode_single_pass(const uint16_t* q_nope, const uint16_t* q_rope,
                            const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
                            int causal, int num_partitions, float* O, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+  return decode_call(q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
                      num_partitions, O, lse, workspace, workspace_bytes, stream, true);
 }
@@ -359,7 +365,7 @@ int mla_decode_splitkv_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
-  return enqueue_split(c, q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, block_table,
+  return enqueue_split(c, q_nope, q_rope, kv_pool, kFormatE4m3, kv_scale, num_pages, block_table,
                        max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
                        lse, false, static_cast<hipStream_t>(stream));
 }
@@ -369,8 +375,8 @@ int mla_decode_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_
                     int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
                     float softmax_scale, int causal, int num_partitions, float* O, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
-                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
+  return decode_call(q_nope, q_rope, kv_pool, kFormatE4m3, kv_scale, num_pages, page_size,
+                     block_table, max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
                      num_partitions, O, lse, workspace, workspace_bytes, stream, false);
 }
 
@@ -381,8 +387,8 @@ int mla_decode_single_pass_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
                                 float softmax_scale, int causal, int num_partitions, float* O,
                                 float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
-                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
+  return decode_call(q_nope, q_rope, kv_pool, kFormatE4m3, kv_scale, num_pages, page_size,
+                     block_table, max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
                      num_partitions, O, lse, workspace, workspace_bytes, stream, true);
 }
 
@@ -393,7 +399,7 @@ int mla_decode_tree(const uint16_t* q_nope, const uint16_t* q_rope, const uint16
                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!tree_mask || (reinterpret_cast<uintptr_t>(tree_mask) & 7)) return MLA_ERR_INVALID_ARG;
   if (Sq > 64) return MLA_ERR_UNSUPPORTED;
-  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+  return decode_call(q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1, num_partitions, O,
                      lse, workspace, workspace_bytes, stream, false, tree_mask);
 }
@@ -406,9 +412,36 @@ int mla_decode_tree_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const u
                          void* workspace, size_t workspace_bytes, void* stream) {
   if (!tree_mask || (reinterpret_cast<uintptr_t>(tree_mask) & 7)) return MLA_ERR_INVALID_ARG;
   if (Sq > 64) return MLA_ERR_UNSUPPORTED;
-  return decode_call(q_nope, q_rope, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
-                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1, num_partitions, O,
-                     lse, workspace, workspace_bytes, stream, false, tree_mask);
+  return decode_call(q_nope, q_rope, kv_pool, kFormatE4m3, kv_scale, num_pages, page_size,
+                     block_table, max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1,
+                     num_partitions, O, lse, workspace, workspace_bytes, stream, false,
+                     tree_mask);
+}
+
+int mla_decode_nope(const uint16_t* q_nope, const uint16_t* kv_pool, int64_t num_pages,
+                    int page_size, const int32_t* block_table, int max_pages_per_seq,
+                    const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                    int causal, int num_partitions, float* O, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  // the rope query is never read for NoPE rows: q_nope stands in for the pointer check
+  return decode_call(q_nope, q_nope, kv_pool, kFormatNope, 1.0f, num_pages, page_size, block_table,
+                     max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
+                     num_partitions, O, lse, workspace, workspace_bytes, stream, false);
+}
+
+int mla_decode_splitkv_nope(const uint16_t* q_nope, const uint16_t* kv_pool, int64_t num_pages,
+                            int page_size, const int32_t* block_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int Sq, int H, float softmax_scale,
+                            int causal, int num_partitions, float* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  Call c;
+  int st = prepare(q_nope, q_nope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                   workspace_bytes, &c);
+  if (st != MLA_OK) return st;
+  return enqueue_split(c, q_nope, q_nope, kv_pool, kFormatNope, 1.0f, num_pages, block_table,
+                       max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
+                       lse, false, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_varlen(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
@@ -417,7 +450,7 @@ int mla_decode_varlen(const uint16_t* q_nope, const uint16_t* q_rope, const uint
                       int B, int Sq, int H, float softmax_scale, int num_partitions, float* O,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q_lens || (reinterpret_cast<uintptr_t>(q_lens) & 3)) return MLA_ERR_INVALID_ARG;
-  return decode_call(q_nope, q_rope, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+  return decode_call(q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, 1, num_partitions, O,
                      lse, workspace, workspace_bytes, stream, false, nullptr, q_lens);
 }
@@ -455,7 +488,7 @@ static int append_call(const uint16_t* kv_new, void* kv_pool, int e4m3, float kv
 int mla_kv_append(const uint16_t* kv_new, uint16_t* kv_pool, int64_t num_pages, int page_size,
                   const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
                   int B, int Sq, void* workspace, size_t workspace_bytes, void* stream) {
-  return append_call(kv_new, kv_pool, 0, 1.0f, num_pages, page_size, block_table,
+  return append_call(kv_new, kv_pool, kFormatBf16, 1.0f, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, workspace, workspace_bytes, stream);
 }
 
@@ -463,7 +496,7 @@ int mla_kv_append_e4m3(const uint16_t* kv_new, uint8_t* kv_pool, float kv_scale,
                        int64_t num_pages, int page_size, const int32_t* block_table,
                        int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return append_call(kv_new, kv_pool, 1, kv_scale, num_pages, page_size, block_table,
+  return append_call(kv_new, kv_pool, kFormatE4m3, kv_scale, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, workspace, workspace_bytes, stream);
 }
 

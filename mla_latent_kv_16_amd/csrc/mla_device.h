@@ -52,6 +52,20 @@ constexpr int kSlotBytes8 = kWaves * kStageCopies8 * 1024;     // 20,480
 constexpr int kStages8 = 6;
 constexpr int kKSteps8 = kQStepsPerWave / 2;                   // 9 sixteen-byte K reads per wave
 
+// NoPE-MLA pools: rows are the 512-wide latent alone (1,024 bf16 bytes, 64 chunks).
+constexpr int kNopeRowBytes = kNope * 2;                       // 1,024
+constexpr int kNopePageBytes = kPage * kNopeRowBytes;          // 65,536
+constexpr int kNopeBlockBytes = kKvBlock * kNopeRowBytes;      // 32,768: half a page
+constexpr int kNopeCopies = kNopeBlockBytes / kWaves / 1024;   // 8 copies of 1 KB per wave
+constexpr int kNopeQSteps = kNope / 16 / 2;                    // 16 MFMA k-steps per wave
+
+// NoPE rows: 16-byte chunk c of row r sits at chunk position c ^ swzn(r), the xor
+// touching the low four chunk bits.  Every 1,024-byte row starts on the same bank,
+// so the xor value must differ across any 16 consecutive rows (the sixteen-byte K
+// reads of 16 rows) and across the 4 rows of a transposed V read: the 4-bit row
+// index rotated by two does both.
+__device__ __forceinline__ int swzn(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -139,9 +153,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // publishes a slot.  M0 is reserved to the compiler, which on gfx9 and later sets
 // it only for instructions these kernels do not use (LDS-DMA builtins, message
 // sends, indirect register indexing), so the asm may overwrite it.  A write of M0
-// needs one wait state before a global load with the LDS bit reads it.  Both are passed through readfirstlane (as unsigned 32-bit
-// halves) so that they are scalar operands even where the compiler cannot prove
-// them uniform.
+// needs one wait state before a global load with the LDS bit reads it.  The base
+// and the LDS address are passed through readfirstlane (as unsigned 32-bit halves)
+// so that they are scalar operands even where the compiler cannot prove them
+// uniform.
 __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
   const uint64_t p = reinterpret_cast<uint64_t>(sbase_in);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));

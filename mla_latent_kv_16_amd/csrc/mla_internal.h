@@ -10,7 +10,8 @@ namespace mla {
 struct SplitArgs {
   const uint16_t* q_nope;      // [B, M, 512] bf16, M = Sq * H folded rows (m = t * H + h)
   const uint16_t* q_rope;      // [B, M, 64]
-  const void* kv_pool;         // [num_pages, 64, 576] bf16, or E4M3 codes when kv_e4m3
+  const void* kv_pool;         // [num_pages, 64, 576] bf16, E4M3 codes when kv_e4m3,
+                               // or [num_pages, 64, 512] bf16 when kv_nope
   const int32_t* block_table;  // [B, max_pages]
   const int32_t* seq_lens;     // [B]
   const uint64_t* tree_mask;   // [B, Sq] draft-tree ancestor bits, or nullptr (a chain)
@@ -29,6 +30,7 @@ struct SplitArgs {
   int slot_rows;               // min(M, M-tile rows)
   int causal;
   int kv_e4m3;                 // 1: the pool holds E4M3 codes scaled by kv_scale
+  int kv_nope;                 // 1: NoPE rows (512 bf16, no rope part; q_rope unused)
   float kv_scale;              // dequantization scale of the pool (1 for bf16)
   float scale_log2;            // softmax_scale * kv_scale * log2(e)
   // Single pass (arrive != nullptr): workgroups past the first n_split merge the

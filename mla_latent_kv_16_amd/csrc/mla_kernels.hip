@@ -222,12 +222,91 @@ __device__ __forceinline__ ReadBases read_bases(int c) {
   return rb;
 }
 
-// ---- the two latent formats ------------------------------------------------------
+// NoPE blocks: wave w copies rows 8 w .. 8 w + 7 of the block (eight copies, one row
+// each); lane l of copy i fetches chunk l ^ swzn(row) of that row into LDS position l.
+struct StageOffsetsN {
+  uint32_t off[kNopeCopies];
+};
+
+__device__ __forceinline__ StageOffsetsN stage_offsets_nope() {
+  StageOffsetsN so;
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kNopeCopies; ++i) {
+    const uint32_t r = 8 * wave + i;
+    so.off[i] = r * kNopeRowBytes + ((lane ^ swzn(r)) << 4);
+  }
+  return so;
+}
+
+__device__ __forceinline__ uint32_t stage_dst_nope(const uint8_t* slot) {
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return lds_addr(slot) + 8 * wave * kNopeRowBytes;
+}
+
+__device__ __forceinline__ void stage_block_nope(const uint8_t* src, uint8_t* slot, int valid,
+                                                 const StageOffsetsN& so) {
+  const uint32_t dst = stage_dst_nope(slot);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (8 * (int)wave + 8 <= valid) {
+#pragma unroll
+    for (int i = 0; i < kNopeCopies; ++i) dma16(src, so.off[i], dst + i * 1024);
+  } else {  // the request's last block: rows past its length re-read row valid - 1
+    const uint32_t lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kNopeCopies; ++i) {
+      const uint32_t r = 8 * wave + i;
+      const uint32_t rs = min(r, (uint32_t)(valid - 1));
+      dma16(src, rs * kNopeRowBytes + ((lane ^ swzn(r)) << 4), dst + i * 1024);
+    }
+  }
+}
+
+// NoPE read bases.  K (A operand of S^T): lane reads row lane % 32 at chunk
+// 32 c + 2 kk + h; the xor covers four chunk bits, so the per-lane part takes one
+// of eight values (kk % 8) and kk / 8 adds 256 bytes.  V (B operand of P V, read
+// transposed): lane 4 r4 + c4 of 16-lane group G addresses row 8 second + 4 h + r4
+// at chunk 32 c + 4 ct + 2 (G % 2) + c4 / 2, byte 8 (c4 % 2); the per-lane part
+// depends on ct % 4 and ct / 4 adds 256 bytes.
+struct ReadBasesN {
+  int k[8];
+  int v[2][4];
+};
+
+__device__ __forceinline__ ReadBasesN read_bases_nope(int c) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  ReadBasesN rb;
+  const int r = lane & 31, sw = swzn(r);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int C = 32 * c + 2 * j + h;
+    rb.k[j] = r * kNopeRowBytes + (((C & ~15) | ((C & 15) ^ sw)) << 4);
+  }
+  const int G = lane >> 4, n = lane & 15, r4 = n >> 2, c4 = n & 3;
+#pragma unroll
+  for (int second = 0; second < 2; ++second) {
+    const int row = 8 * second + 4 * h + r4;
+    const int sw2 = swzn(row);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int C = 32 * c + 4 * (q & 1) + 8 * (q >> 1) + 2 * (G & 1) + (c4 >> 1);
+      rb.v[second][q] = row * kNopeRowBytes + (((C & ~15) | ((C & 15) ^ sw2)) << 4) + 8 * (c4 & 1);
+    }
+  }
+  return rb;
+}
+
+// ---- the latent formats ----------------------------------------------------------
 // Everything that depends on how a pool row is stored: bf16 (1,152-byte rows, 36 KB
-// blocks, a four-slot ring) or E4M3 with a per-tensor scale (576-byte rows, 18 KB
-// blocks in 20 KB slots, a six-slot ring).  The scores and P V run on bf16 MFMAs in
-// both cases: E4M3 operands are widened exactly in registers after the LDS read.
+// blocks, a four-slot ring), E4M3 with a per-tensor scale (576-byte rows, 18 KB
+// blocks in 20 KB slots, a six-slot ring) or NoPE bf16 (the 512-wide latent alone:
+// 1,024-byte rows, 32 KB blocks, a four-slot ring, 16 k-steps per wave).  The
+// scores and P V run on bf16 MFMAs in every case: E4M3 operands are widened exactly
+// in registers after the LDS read.
 struct Bf16Kv {
+  static constexpr int kQSteps = kQStepsPerWave;  // MFMA k-steps per wave
+  static constexpr bool kRopeQ = true;            // queries have a q_rope part
   static constexpr int kStagesN = kStages;        // ring slots
   static constexpr int kSlot = kStageBytes;       // bytes per slot
   static constexpr int kCopies = kStageCopiesPerWave;
@@ -252,6 +331,8 @@ struct Bf16Kv {
 };
 
 struct E4m3Kv {
+  static constexpr int kQSteps = kQStepsPerWave;
+  static constexpr bool kRopeQ = true;
   static constexpr int kStagesN = kStages8;
   static constexpr int kSlot = kSlotBytes8;
   static constexpr int kCopies = kStageCopies8;
@@ -272,7 +353,31 @@ struct E4m3Kv {
   }
 };
 
-// A-operand (K) stream of S^T for one block: operands for k-steps 0..17 in order,
+struct NopeKv {
+  static constexpr int kQSteps = kNopeQSteps;
+  static constexpr bool kRopeQ = false;
+  static constexpr int kStagesN = kStages;
+  static constexpr int kSlot = kNopeBlockBytes;
+  static constexpr int kCopies = kNopeCopies;
+  static constexpr int kPageB = kNopePageBytes;
+  static constexpr int kHalfB = kNopeBlockBytes;
+  using Offsets = StageOffsetsN;
+  using Bases = ReadBasesN;
+  static __device__ __forceinline__ Offsets offsets() { return stage_offsets_nope(); }
+  static __device__ __forceinline__ Bases bases(int c) { return read_bases_nope(c); }
+  static __device__ __forceinline__ void stage(const uint8_t* src, uint8_t* slot, int valid,
+                                               const Offsets& so) {
+    stage_block_nope(src, slot, valid, so);
+  }
+  static __device__ __forceinline__ uint32_t dst(const uint8_t* slot) {
+    return stage_dst_nope(slot);
+  }
+  static __device__ __forceinline__ int q_k(int c, int kk, int h) {
+    return (kNopeQSteps * c + kk) * 16 + 8 * h;
+  }
+};
+
+// A-operand (K) stream of S^T for one block: operands for k-steps 0..kQSteps-1 in order,
 // with LDS reads running ahead of the MFMAs.
 template <class Kv> struct KStream;
 
@@ -370,6 +475,53 @@ template <> struct VStream<E4m3Kv> {
   }
 };
 
+template <> struct KStream<NopeKv> {
+  static constexpr int DQ = 4;  // reads in flight
+  const uint8_t* blk;
+  const ReadBasesN* rb;
+  bf16x8 buf[DQ];
+  __device__ __forceinline__ bf16x8 rd(int kk) const {
+    return lds_read_b128(blk + rb->k[kk & 7], (kk >> 3) * 256);
+  }
+  __device__ __forceinline__ void start() {
+#pragma unroll
+    for (int u = 0; u < DQ; ++u) buf[u] = rd(u);
+  }
+  __device__ __forceinline__ bf16x8 next(int kk) {
+    const bf16x8 a = buf[kk % DQ];
+    if (kk + DQ < kNopeQSteps) buf[kk % DQ] = rd(kk + DQ);
+    return a;
+  }
+};
+
+template <> struct VStream<NopeKv> {
+  static constexpr int DV = 4;  // read pairs in flight
+  const uint8_t* blk;
+  const ReadBasesN* rb;
+  bf16x4 b0[DV], b1[DV];
+  __device__ __forceinline__ bf16x4 rd(int t, int sd) const {
+    const int ks = t >> 3, ct = t & 7;
+    return lds_read_tr(blk + rb->v[sd][ct & 3], (ct >> 2) * 256 + ks * 16 * kNopeRowBytes);
+  }
+  __device__ __forceinline__ void start() {
+#pragma unroll
+    for (int u = 0; u < DV; ++u) {
+      b0[u] = rd(u, 0);
+      b1[u] = rd(u, 1);
+    }
+  }
+  __device__ __forceinline__ bf16x8 next(int t) {
+    const int u = t % DV;
+    const bf16x8 v = {b0[u][0], b0[u][1], b0[u][2], b0[u][3],
+                      b1[u][0], b1[u][1], b1[u][2], b1[u][3]};
+    if (t + DV < 2 * kColTilesPerWave) {
+      b0[u] = rd(t + DV, 0);
+      b1[u] = rd(t + DV, 1);
+    }
+    return v;
+  }
+};
+
 // ---- block copies issued from inside the pipeline step -------------------------
 // The vector memory path takes a wave's copies of a block only at its own pace
 // (hundreds of cycles), so the step issues them one per two S^T MFMAs instead of in
@@ -406,7 +558,7 @@ __device__ __forceinline__ f32x16 qk_partial(const uint8_t* blk, const typename 
   ks.start();
   f32x16 s0 = {};
 #pragma unroll
-  for (int kk = 0; kk < kQStepsPerWave; ++kk) {
+  for (int kk = 0; kk < Kv::kQSteps; ++kk) {
     s0 = mfma32(ks.next(kk), qreg[kk], s0);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -452,7 +604,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
 
   // ---- S^T of block i + 1 on the MFMA pipe, the softmax step of block i in between
 #pragma unroll
-  for (int kk = 0; kk < kQStepsPerWave; ++kk) {
+  for (int kk = 0; kk < Kv::kQSteps; ++kk) {
     if constexpr (HAS_NEXT) {
       n0 = mfma32(kst.next(kk), qreg[kk], n0);
       if ((kk & 1) && (kk >> 1) < Kv::kCopies)
@@ -517,7 +669,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
     } else if (kk == 12) {
       vst.start();  // the first V operands of block i
     }
-    if (HAS_NEXT && kk == kQStepsPerWave - 1) __syncthreads();  // block i's halves are read
+    if (HAS_NEXT && kk == Kv::kQSteps - 1) __syncthreads();  // block i's halves are read
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -671,17 +823,17 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query row m_q, for k-step kk the
   // eight query elements from k = Kv::q_k(c, kk, lane / 32)
-  bf16x8 qreg[kQStepsPerWave];
+  bf16x8 qreg[Kv::kQSteps];
   {
     const int h = lane >> 5;
     const size_t qrow = (size_t)b * M + (q_ok ? m_q : 0);
 #pragma unroll
-    for (int kk = 0; kk < kQStepsPerWave; ++kk) {
+    for (int kk = 0; kk < Kv::kQSteps; ++kk) {
       const int k0 = Kv::q_k(c, kk, h);
       bf16x8 v;
-      if (k0 < kNope)
+      if (!Kv::kRopeQ || k0 < kNope)
         v = *reinterpret_cast<const bf16x8*>(a.q_nope + qrow * kNope + k0);
-      else
+      else if constexpr (Kv::kRopeQ)
         v = *reinterpret_cast<const bf16x8*>(a.q_rope + qrow * kRope + (k0 - kNope));
       qreg[kk] = q_ok ? v : bf16x8{};
     }
@@ -1206,7 +1358,9 @@ hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream) {
     nwg += a.comb_rows == 0 ? rows : (rows + per - 1) / per;
   }
   if (n_split != a.n_split || nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.kv_e4m3)
+  if (a.kv_nope)
+    hipLaunchKernelGGL(splitkv_kernel<NopeKv>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+  else if (a.kv_e4m3)
     hipLaunchKernelGGL(splitkv_kernel<E4m3Kv>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(splitkv_kernel<Bf16Kv>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);

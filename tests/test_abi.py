@@ -22,6 +22,7 @@ def test_library_exports_every_header_function():
     names = mla.header_functions()
     assert names == sorted([
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
+        "mla_decode_nope", "mla_decode_splitkv_nope",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
         "mla_decode_splitkv_e4m3", "mla_decode_tree", "mla_decode_tree_e4m3",
         "mla_decode_varlen", "mla_decode_workspace_size", "mla_kv_append", "mla_kv_append_e4m3", "mla_prefill_with_prefix", "mla_read_error_flags",
