@@ -22,5 +22,7 @@ from .mla_oracle import (  # noqa: F401
     mla_attention_varlen,
     e4m3_quantize,
     mla_attention_nope,
+    absorb_q,
+    project_o,
     kv_append,
 )

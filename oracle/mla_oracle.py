@@ -416,6 +416,21 @@ def mla_attention_nope(q_nope, pool, block_table, seq_lens, scale, causal=True, 
     return O.reshape(B, Sq, H, NOPE), LSE.reshape(B, Sq, H)
 
 
+def absorb_q(q_heads, w_uk_t):
+    """The query with the key up-projection absorbed (TokenSpeed review page, Attack 1:
+    "absorb" before the latent attention): q_lat[b,t,h,c] = sum_k q_heads[b,t,h,k] *
+    W_UK[h][k][c], with w_uk_t[h, c, k] = W_UK[h][k][c].  q_heads [B,Sq,H,128]
+    (bf16 bits or floats), w_uk_t [H,512,128].  Returns fp64 [B,Sq,H,512]."""
+    return np.einsum("bthk,hck->bthc", _f64(q_heads), _f64(w_uk_t))
+
+
+def project_o(O, w_uv):
+    """The value up-projection applied to the latent output (the "project" after the
+    attention): out[b,t,h,v] = sum_c O[b,t,h,c] * W_UV[h][v][c].  O [B,Sq,H,512]
+    (floats), w_uv [H,128,512] (bf16 bits or floats).  Returns fp64 [B,Sq,H,128]."""
+    return np.einsum("bthc,hvc->bthv", np.asarray(O, dtype=np.float64), _f64(w_uv))
+
+
 def lse_merge(parts):
     """Merge split partials [(O_s, LSE_s), ...] into (O, LSE).
 
