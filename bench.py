@@ -177,7 +177,7 @@ def main():
     import numpy as np
     import torch
     import mla_latent_kv_16_amd as mla
-    from mla_latent_kv_16_amd.workloads import make_workload
+    from mla_latent_kv_16_amd.workloads import f32_to_bf16_bits, make_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -289,7 +289,6 @@ def main():
     # takes 576-wide rows, so NoPE pools skip it.
     append_us = append_bytes = None
     if not args.nope:
-        from mla_latent_kv_16_amd.workloads import f32_to_bf16_bits
         kv_new = torch.from_numpy(f32_to_bf16_bits(np.random.default_rng(1).standard_normal(
             (w.B, w.Sq, 576)).astype(np.float32)).view(np.int16)).to(dev)
         app_ws = torch.zeros(256, dtype=torch.uint8, device=dev)
@@ -307,6 +306,32 @@ def main():
         if mla.read_error_flags(app_ws):
             raise SystemExit("kv append reported a data fault flag")
         append_bytes = w.B * w.Sq * 576 * (2 + w.row_bytes // 576)
+
+    # The GEMMs around the attention for this batch's shape (absorb before, project
+    # after), with seeded random weights, timed back to back.
+    gemm = {}
+    if not args.nope:
+        g_rng = np.random.default_rng(2)
+        bfw = lambda shape, sc: torch.from_numpy(f32_to_bf16_bits(
+            (g_rng.standard_normal(shape) * sc).astype(np.float32)).view(np.int16)).to(dev)
+        q_heads = bfw((w.B, w.Sq, w.H, 128), 1.0)
+        w_uk_t, w_uv = bfw((w.H, 512, 128), 128 ** -0.5), bfw((w.H, 128, 512), 512 ** -0.5)
+        q_lat = torch.empty((w.B, w.Sq, w.H, 512), dtype=torch.int16, device=dev)
+        o_proj = torch.empty((w.B, w.Sq, w.H, 128), dtype=torch.float32, device=dev)
+        rows_h = w.B * w.Sq * w.H
+        for tag, (fn, _) in (("absorb", mla.bound_absorb_q(q_heads, w_uk_t, q_lat)),
+                             ("project", mla.bound_project_o(O, w_uv, o_proj))):
+            fn()
+            gev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            torch.cuda.synchronize()
+            gev[0].record()
+            for _ in range(20):
+                fn()
+            gev[1].record()
+            torch.cuda.synchronize()
+            us = gev[0].elapsed_time(gev[1]) / 20 * 1e3
+            gemm[f"{tag}_us"] = round(us, 2)
+            gemm[f"{tag}_TFLOPs"] = round(2 * rows_h * 128 * 512 / (us * 1e-6) / 1e12, 2)
 
     peaks = None if args.no_measured_peaks else measured_peaks(torch, dev)
 
@@ -376,6 +401,7 @@ def main():
         "kv_append_us": None if append_us is None else round(append_us, 2),
         "kv_append_GBps": (None if append_us is None
                            else round(append_bytes / (append_us * 1e-6) / 1e9, 2)),
+        "absorb_project": gemm or None,
         "roofline": roof,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,

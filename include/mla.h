@@ -309,6 +309,34 @@ int mla_kv_append_e4m3(const uint16_t* kv_new, uint8_t* kv_pool, float kv_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The per-head GEMMs that bracket the latent attention (TokenSpeed review page,
+ * Attack 1: "absorb + project").  Per-head widths are 128 (the unabsorbed query
+ * part and the projected values; the softmax scale (128 + 64)^-0.5 of the
+ * configurations).  Both run on bf16 MFMA with fp32 accumulation; rows are the
+ * B * Sq (request, draft) pairs.
+ *
+ * mla_absorb_q: q_lat[b,t,h,c] = sum_k q_heads[b,t,h,k] * W_UK[h][k][c], rounded to
+ * bf16 (nearest, ties to even) -- the q_nope that mla_decode takes.
+ *   q_heads  bf16 [B, Sq, H, 128]
+ *   w_uk_t   bf16 [H, 512, 128]: element [h][c][k] = W_UK[h][k][c] (W_UK of each head
+ *            transposed once, so that every 128-long k run is contiguous)
+ *   q_lat    bf16 [B, Sq, H, 512] (written)
+ *
+ * mla_project_o: out[b,t,h,v] = sum_c O[b,t,h,c] * W_UV[h][v][c], with O rounded to
+ * bf16 for the MFMA and the sum kept in fp32.
+ *   O        fp32 [B, Sq, H, 512] (mla_decode's output)
+ *   w_uv     bf16 [H, 128, 512]: element [h][v][c] = W_UV[h][v][c]
+ *   out      fp32 [B, Sq, H, 128] (written)
+ *
+ * Pointers are 16-byte aligned device memory; B, Sq, H >= 1 (B * Sq <= 2^24,
+ * H <= 65535).  Each only enqueues one kernel on `stream`.
+ */
+int mla_absorb_q(const uint16_t* q_heads, const uint16_t* w_uk_t, uint16_t* q_lat, int B, int Sq,
+                 int H, void* stream);
+int mla_project_o(const float* O, const uint16_t* w_uv, float* out, int B, int Sq, int H,
+                  void* stream);
+
+/*
  * Waits for `stream`, then copies the workspace header's error flags
  * (MLA_FLAG_*) to *flags and clears them.  Reading forces a synchronisation, so
  * callers use it in checked runs and tests, not on the hot path.

@@ -7,6 +7,10 @@ Importing this package loads nothing; the library is opened on first use.
 """
 from ._binding import (  # noqa: F401
     BoundDecode,
+    bound_absorb_q,
+    bound_project_o,
+    absorb_q,
+    project_o,
     bound_kv_append,
     MLAError,
     LIB_PATH,

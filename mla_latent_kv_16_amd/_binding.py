@@ -54,6 +54,8 @@ _SIGNATURES = {
                          _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_splitkv_nope": ([_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
                                  _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "mla_absorb_q": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp], _i32),
+    "mla_project_o": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp], _i32),
     "mla_decode_varlen": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
                            _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_tree": ([_vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
@@ -303,6 +305,61 @@ def decode_nope(q_nope, kv_pool, block_table, seq_lens, softmax_scale, causal=Tr
                                _stream_handle(stream))
     _check(st, "mla_decode_nope")
     return out, lse
+
+
+def absorb_q(q_heads, w_uk_t, out=None, stream=None):
+    """mla_absorb_q: q_heads bf16 [B, Sq, H, 128], w_uk_t bf16 [H, 512, 128] ->
+    q_lat bf16 [B, Sq, H, 512] (the absorbed query mla_decode takes)."""
+    call, out = bound_absorb_q(q_heads, w_uk_t, out, stream)
+    call()
+    return out
+
+
+def bound_absorb_q(q_heads, w_uk_t, out=None, stream=None):
+    """absorb_q checked and marshalled once: returns (callable, out)."""
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16)
+    if q_heads.dim() != 4 or q_heads.shape[3] != 128:
+        raise ValueError("q_heads must be [B, Sq, H, 128]")
+    B, Sq, H = q_heads.shape[:3]
+    _expect(q_heads, "q_heads", bf)
+    _expect(w_uk_t, "w_uk_t", bf, (H, 512, 128))
+    if out is None:
+        out = torch.empty((B, Sq, H, 512), dtype=q_heads.dtype, device=q_heads.device)
+    _expect(out, "out", bf, (B, Sq, H, 512))
+    fn, args = lib().mla_absorb_q, (_ptr(q_heads), _ptr(w_uk_t), _ptr(out), B, Sq, H,
+                                    _stream_handle(stream))
+
+    def call(_keep=(q_heads, w_uk_t, out)):
+        _check(fn(*args), "mla_absorb_q")
+    return call, out
+
+
+def project_o(O, w_uv, out=None, stream=None):
+    """mla_project_o: O fp32 [B, Sq, H, 512], w_uv bf16 [H, 128, 512] ->
+    fp32 [B, Sq, H, 128]."""
+    call, out = bound_project_o(O, w_uv, out, stream)
+    call()
+    return out
+
+
+def bound_project_o(O, w_uv, out=None, stream=None):
+    """project_o checked and marshalled once: returns (callable, out)."""
+    torch = _torch()
+    if O.dim() != 4 or O.shape[3] != 512:
+        raise ValueError("O must be [B, Sq, H, 512]")
+    B, Sq, H = O.shape[:3]
+    _expect(O, "O", (torch.float32,))
+    _expect(w_uv, "w_uv", (torch.bfloat16, torch.int16), (H, 128, 512))
+    if out is None:
+        out = torch.empty((B, Sq, H, 128), dtype=torch.float32, device=O.device)
+    _expect(out, "out", (torch.float32,), (B, Sq, H, 128))
+    fn, args = lib().mla_project_o, (_ptr(O), _ptr(w_uv), _ptr(out), B, Sq, H,
+                                     _stream_handle(stream))
+
+    def call(_keep=(O, w_uv, out)):
+        _check(fn(*args), "mla_project_o")
+    return call, out
 
 
 def decode_varlen(q_nope, q_rope, kv_pool, block_table, seq_lens, q_lens, softmax_scale,

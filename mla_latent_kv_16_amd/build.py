@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_api.hip", "mla_kernels.hip", "mla_append.hip"]
+SOURCES = ["mla_api.hip", "mla_kernels.hip", "mla_append.hip", "mla_project.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -500,6 +500,29 @@ int mla_kv_append_e4m3(const uint16_t* kv_new, uint8_t* kv_pool, float kv_scale,
                      max_pages_per_seq, seq_lens, B, Sq, workspace, workspace_bytes, stream);
 }
 
+int mla_absorb_q(const uint16_t* q_heads, const uint16_t* w_uk_t, uint16_t* q_lat, int B, int Sq,
+                 int H, void* stream) {
+  if (!q_heads || !w_uk_t || !q_lat) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_heads) || !aligned16(w_uk_t) || !aligned16(q_lat)) return MLA_ERR_INVALID_ARG;
+  if (B < 1 || Sq < 1 || H < 1) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)B * Sq > (1 << 24) || H > 65535) return MLA_ERR_UNSUPPORTED;
+  return launch_absorb(q_heads, w_uk_t, q_lat, B * Sq, H, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_project_o(const float* O, const uint16_t* w_uv, float* out, int B, int Sq, int H,
+                  void* stream) {
+  if (!O || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(O) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (B < 1 || Sq < 1 || H < 1) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)B * Sq > (1 << 24) || H > 65535) return MLA_ERR_UNSUPPORTED;
+  return launch_project(O, w_uv, out, B * Sq, H, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {
   if (!workspace || !flags) return MLA_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);

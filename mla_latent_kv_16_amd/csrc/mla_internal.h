@@ -72,6 +72,15 @@ struct AppendArgs {
   float inv_scale;             // fp32(1 / kv_scale) for E4M3 pools
 };
 
+// Absorb / project GEMMs around the attention: per-head width of the unabsorbed
+// query and of the projected values (128, as in the 192^-0.5 = (128 + 64)^-0.5 scale).
+constexpr int kHeadDim = 128;
+constexpr int kProjThreads = 256;
+hipError_t launch_absorb(const uint16_t* q_heads, const uint16_t* w_uk_t, uint16_t* q_lat,
+                         int rows, int H, hipStream_t stream);
+hipError_t launch_project(const float* O, const uint16_t* w_uv, float* out, int rows, int H,
+                          hipStream_t stream);
+
 // Launch helpers (defined next to the kernels).
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);

@@ -21,6 +21,7 @@ FAKE = 0x10000  # 16-byte aligned host address; never dereferenced by the host c
 def test_library_exports_every_header_function():
     names = mla.header_functions()
     assert names == sorted([
+        "mla_absorb_q", "mla_project_o",
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
         "mla_decode_nope", "mla_decode_splitkv_nope",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
@@ -183,6 +184,17 @@ def test_kv_append_rejects_on_host(over, code):
     if "scale" not in over:
         assert L.mla_kv_append(a["new"], a["pool"], 16, *common) == code
     assert L.mla_kv_append_e4m3(a["new"], a["pool"], a["scale"], 16, *common) == code
+
+
+@pytest.mark.parametrize("name", ["mla_absorb_q", "mla_project_o"])
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, 1, 1, 1), INVALID), ((FAKE, None, FAKE, 1, 1, 1), INVALID),
+    ((FAKE, FAKE, None, 1, 1, 1), INVALID), ((FAKE + 8, FAKE, FAKE, 1, 1, 1), INVALID),
+    ((FAKE, FAKE, FAKE, 0, 1, 1), INVALID), ((FAKE, FAKE, FAKE, 1, 0, 1), INVALID),
+    ((FAKE, FAKE, FAKE, 1, 1, 0), INVALID), ((FAKE, FAKE, FAKE, 1, 1, 70000), UNSUPPORTED),
+])
+def test_gemms_reject_on_host(name, args, code):
+    assert getattr(mla.lib(), name)(*args, None) == code
 
 
 def test_tree_e4m3_rejects_bad_scale():
