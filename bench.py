@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the copy / matmul measurement of achievable peaks")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed steps")
     ap.add_argument("--no-single-pass", action="store_true",
                     help="skip the one-launch comparison (profiler runs: every split-KV kernel "
                          "launch is then a split pass alone)")
@@ -262,6 +264,33 @@ def main():
     kev[1].record()
     torch.cuda.synchronize()
     split_b2b = kev[0].elapsed_time(kev[1]) / args.steps
+
+    # The same steps replayed from HIP graphs (one captured step per pool copy), as a
+    # serving loop that captures its decode step would run them.
+    graph_us = None
+    if not args.no_graph:
+        gs = torch.cuda.Stream()
+        gcalls = [mla.BoundDecode(q_nope, q_rope, pool, bt, sl, scale, w.causal, G, O, lse, ws,
+                                  stream=gs, kv_scale=kv_scale, nope=args.nope) for pool in pools]
+        graphs = []
+        with torch.cuda.stream(gs):
+            for c in gcalls:
+                c()
+        torch.cuda.synchronize()
+        for c in gcalls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                c()
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % n_copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % n_copies].replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t0) * 1e6 / args.steps
+        del graphs, gcalls
 
     # The same steps in one launch each (mla_decode_single_pass), for comparison.
     single_pass_us = None
@@ -395,6 +424,7 @@ def main():
         "split_pass_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
                                   round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
         "split_kernel_us_back_to_back": round(split_b2b * 1e3, 2),
+        "us_per_step_graph_replay": None if graph_us is None else round(graph_us, 2),
         "single_pass_us_per_step": None if single_pass_us is None else round(single_pass_us, 2),
         "split_pass_hbm_frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
         "split_pass_mfma_frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
