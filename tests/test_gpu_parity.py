@@ -234,6 +234,22 @@ def test_single_pass_counters_return_to_zero_and_workspace_is_reusable():
     assert mla.read_error_flags(ws) == 0
 
 
+@pytest.mark.parametrize("single", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("parts", [0, 300, 2100], ids=["G=auto", "G=300", "G=2100"])
+def test_maximum_batch(parts, single):
+    """B = 1024 (the library's limit) with short, ragged contexts: the page-prefix scan
+    covers sixteen requests per lane and the merges sum pages over the whole batch."""
+    w = make_workload("tiny", seed=140, B=1024, Sq=2, H=16, lens=("uniform", 2, 260))
+    O, lse = run(w, parts=parts, fn=mla.decode_single_pass if single else None)
+    check(O, lse, *oracle(w), f"B=1024 parts={parts} single={single}")
+
+
+def test_batch_over_the_limit_is_rejected():
+    w = make_workload("tiny", seed=141, B=1025, Sq=1, H=16, lens=("fixed", 64))
+    with pytest.raises(mla.MLAError):
+        run(w)
+
+
 def test_prefill_entry_point_small():
     w = make_workload("tiny", seed=114, B=1, Sq=96, H=16, lens=("fixed", 64 * 20 + 96))
     O, lse = run(w, fn=mla.prefill_with_prefix)
