@@ -147,7 +147,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed steps first: the clocks take about 25 ms of load to settle")
     ap.add_argument("--config", default="spec4",
                     help="tiny | spec4 | spec8 | spec16 | sweep | prefill")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "e4m3"],
