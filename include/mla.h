@@ -164,6 +164,33 @@ int mla_decode_combine(const int32_t* seq_lens, int max_pages_per_seq, int B, in
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_splitkv plus a record of where its workgroups ran.  The GPU hands
+ * workgroups to its eight XCDs round-robin, and an XCD's L2 serves only that XCD;
+ * keeping the workgroups that share KV pages on one XCD is what keeps the L2 hit
+ * rate up (TokenSpeed review page, "Optimizing Attention on MI300X" entry and the
+ * Fleet entry on chiplet-aware L2 reuse).  The split pass numbers its workgroups so
+ * that the M-tiles of one KV partition, and neighbouring partitions, share an XCD
+ * (with one partition, where all M-tiles read the same pages, workgroup w instead
+ * takes M-tile n - 1 - w of n, the causally longest first, spread over every XCD);
+ * this entry point lets a caller check that on the device at hand.
+ *   wg_trace      int32 device buffer; split-KV workgroup w (launch order,
+ *                 0 <= w < num_partitions_used * ceil(Sq * H / 64)) writes
+ *                 wg_trace[3 w] = the XCC id register of the XCD it ran on,
+ *                 wg_trace[3 w + 1] = its KV partition, wg_trace[3 w + 2] = its M-tile
+ *   wg_trace_len  entries available; fewer than 3 per workgroup -> MLA_ERR_INVALID_ARG
+ *                 (as is a NULL or misaligned wg_trace), before anything is enqueued
+ * Every other argument, and O, lse and the workspace contents, exactly as for
+ * mla_decode_splitkv (the record changes no result).
+ */
+int mla_decode_splitkv_placement(const uint16_t* q_nope, const uint16_t* q_rope,
+                                 const uint16_t* kv_pool, int64_t num_pages, int page_size,
+                                 const int32_t* block_table, int max_pages_per_seq,
+                                 const int32_t* seq_lens, int B, int Sq, int H,
+                                 float softmax_scale, int causal, int num_partitions,
+                                 float* O, float* lse, void* workspace, size_t workspace_bytes,
+                                 int32_t* wg_trace, int64_t wg_trace_len, void* stream);
+
+/*
  * Chunked prefill on top of a long cached prefix (atlas §11 Chunked prefill;
  * TokenSpeed launch news, prefill-kernel paragraph).  Sq is the chunk length,
  * seq_lens[b] = cached prefix + chunk, and the chunk's own latent rows are already

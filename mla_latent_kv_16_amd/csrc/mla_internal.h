@@ -41,6 +41,9 @@ struct SplitArgs {
   uint32_t* done;              // [B * n_mt]
   int n_split;                 // split-KV workgroups (G * n_mt)
   int comb_rows;               // single pass: 0 = a workgroup per row, else rows per wave
+  // Placement record (or nullptr): split-KV workgroup w writes its XCD (the hardware
+  // XCC id), partition and M-tile to wg_trace[3 w .. 3 w + 2].
+  int32_t* wg_trace;           // [n_split, 3]
 };
 
 struct CombineArgs {

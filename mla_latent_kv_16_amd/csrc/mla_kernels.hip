@@ -1272,9 +1272,23 @@ splitkv_kernel(SplitArgs a) {
     merge_role(a, (int)blockIdx.x - a.n_split, ring);
     return;
   }
-  const int lam = xcd_logical_id(blockIdx.x, a.n_split);
+  // With several partitions, the M-tiles of one partition (and neighbouring
+  // partitions) share an XCD and its L2.  With one partition every M-tile walks the
+  // same pages anyway; launch order then spreads the causally longer last M-tiles
+  // over all eight XCDs, heaviest first, instead of giving them all to one.
+  const int lam = a.G > 1 ? xcd_logical_id(blockIdx.x, a.n_split)
+                          : a.n_split - 1 - (int)blockIdx.x;
   const int g = lam / a.n_mt;
   const int mt = lam - g * a.n_mt;
+  if (a.wg_trace && threadIdx.x == 0) {
+    // where this workgroup actually runs: the XCC id register of the executing die
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+    int32_t* rec = a.wg_trace + 3 * (size_t)blockIdx.x;
+    rec[0] = (int32_t)xcc;
+    rec[1] = g;
+    rec[2] = mt;
+  }
 
   // page prefix and clamped lengths of the batch, in the exchange buffer until the
   // first piece starts

@@ -25,7 +25,8 @@ def test_library_exports_every_header_function():
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
         "mla_decode_nope", "mla_decode_splitkv_nope",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
-        "mla_decode_splitkv_e4m3", "mla_decode_tree", "mla_decode_tree_e4m3",
+        "mla_decode_splitkv_e4m3", "mla_decode_splitkv_placement", "mla_decode_tree",
+        "mla_decode_tree_e4m3",
         "mla_decode_varlen", "mla_decode_workspace_size", "mla_kv_append", "mla_kv_append_e4m3", "mla_prefill_with_prefix", "mla_read_error_flags",
         "mla_status_string"])
     L = mla.lib()
@@ -217,6 +218,23 @@ def test_combine_rejects_on_host():
     assert f(FAKE, 4, 0, 1, 16, 2, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
     assert f(FAKE, 4, 1, 1, 16, 2, FAKE, FAKE, None, 1 << 20, None) == WORKSPACE
     assert f(FAKE, 4, 1, 1, 16, 2, FAKE, FAKE, FAKE, 10, None) == WORKSPACE
+
+
+def test_placement_record_rejects_on_host():
+    """The placement record needs 3 int32 per split-KV workgroup (G x M-tiles), and an
+    aligned, non-null buffer; any shortfall is refused before anything is enqueued."""
+    f = mla.lib().mla_decode_splitkv_placement
+
+    def call(trace, n, B=4, Sq=16, H=16, parts=8):
+        return f(FAKE, FAKE, FAKE, 64, 64, FAKE, 16, FAKE, B, Sq, H, 0.07, 1, parts, FAKE, FAKE,
+                 FAKE, 1 << 30, trace, n, None)
+    # Sq * H = 256 folded rows: 4 M-tiles of 64, so 8 partitions run 32 workgroups
+    assert call(FAKE, 3 * 32 - 1) == INVALID
+    assert call(None, 3 * 32) == INVALID
+    assert call(FAKE + 2, 3 * 32) == INVALID
+    assert call(FAKE, 3 * 32, parts=-1) == INVALID
+    assert call(FAKE, 3 * 32, B=0) == INVALID
+    assert call(FAKE, 3 * 8 - 1, Sq=4, parts=8) == INVALID  # one M-tile: 8 workgroups
 
 
 def test_read_error_flags_rejects_null():
