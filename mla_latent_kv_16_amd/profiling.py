@@ -4,6 +4,7 @@
     python -m mla_latent_kv_16_amd.profiling traffic <fetch_counter.csv> <write_counter.csv>
                                                      <workload> <out.json> "<commands>"
     python -m mla_latent_kv_16_amd.profiling counters <out.md> "<commands>" <counter.csv>...
+    python -m mla_latent_kv_16_amd.profiling table    <bench.jsonl> <out.md> "<commands>"
 
 `stats` keeps the per-kernel table of a `--kernel-trace --stats` run.  `traffic`
 turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of `bench.py --copy-probe`
@@ -128,6 +129,29 @@ def counters_table(paths) -> str:
     return "\n".join(out)
 
 
+def bench_table(jsonl: str) -> str:
+    """One markdown row per bench.py JSON line (as printed by bench.py)."""
+    out = ["| workload | KV | µs/step | graph µs/step | KV-read rate per step | split (events) µs "
+           "| split b2b µs | single pass µs/step | bound | split kernel achieved | of measured "
+           "| CPU oracle |",
+           "|" + "---|" * 12]
+    with open(jsonl) as f:
+        recs = [json.loads(ln) for ln in f if ln.startswith("{")]
+    for r in recs:
+        c, rf, cpu = r["config"], r["roofline"], r.get("cpu_baseline")
+        kv = "e4m3" if "e4m3" in c["latent"] else ("nope" if "NoPE" in c["latent"] else "bf16")
+        fmt = lambda v: "—" if v is None else f"{v}"
+        unit = rf["unit"]
+        ach = f"{rf['achieved']} {unit} ({rf['frac']:.1%})"
+        cpu_s = f"{cpu['value']:.4g} {cpu['unit']} on {cpu['cores']} threads" if cpu else "—"
+        out.append(
+            f"| {c['workload']} | {kv} | {r['us_per_step']} | {fmt(r.get('us_per_step_graph_replay'))} "
+            f"| {r['value']} GB/s ({r['kv_frac_of_hbm_peak']:.1%} of 8 TB/s) | {r['split_pass_us']} "
+            f"| {r['split_kernel_us_back_to_back']} | {fmt(r.get('single_pass_us_per_step'))} "
+            f"| {rf['bound']} | {ach} | {rf.get('frac_of_measured_peak', 0):.0%} | {cpu_s} |")
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         src, dst, cmd = argv[1], argv[2], argv[3]
@@ -147,6 +171,16 @@ def main(argv):
             f.write(f"# Hardware counters\n\nCommands:\n\n```\n{cmd}\n```\n\n")
             f.write(f"Kernel sources hash: `{kernel_hash()}`\n\n")
             f.write(counters_table(argv[3:]) + "\n")
+        print(dst)
+    elif len(argv) >= 4 and argv[0] == "table":
+        src, dst, cmd = argv[1], argv[2], argv[3]
+        with open(dst, "w") as f:
+            f.write(f"# bench.py on every workload\n\nCommand (one per line of the table):\n\n"
+                    f"```\n{cmd}\n```\n\nKernel sources hash: `{kernel_hash()}`\n\n")
+            f.write(bench_table(src) + "\n\nRaw JSON lines:\n\n```\n")
+            with open(src) as g:
+                f.write("".join(ln for ln in g if ln.startswith("{")))
+            f.write("```\n")
         print(dst)
     else:
         print(__doc__)
