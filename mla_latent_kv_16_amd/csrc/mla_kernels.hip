@@ -422,17 +422,18 @@ template <> struct KStream<E4m3Kv> {
   }
 };
 
-// B-operand (V) stream of O = P V for one block: operands for MFMA t = 8 ks + ct
-// (k-step ks of 16 kv rows, column tile ct of the wave's 256 columns).
-template <class Kv> struct VStream;
+// B-operand (V) stream of O = P V for one block: operands for MFMA t, which takes
+// k-step ks = (t / 8) ^ F (16 kv rows) and column tile ct = t % 8 of the wave's 256
+// columns.  F = 1 runs the block's second k-step first.
+template <class Kv, int F> struct VStream;
 
-template <> struct VStream<Bf16Kv> {
+template <int F> struct VStream<Bf16Kv, F> {
   static constexpr int DV = 4;  // read pairs in flight
   const uint8_t* blk;
   const ReadBases* rb;
   bf16x4 b0[DV], b1[DV];
   __device__ __forceinline__ bf16x4 rd(int t, int sd) const {
-    const int ks = t >> 3, ct = t & 7;
+    const int ks = (t >> 3) ^ F, ct = t & 7;
     return lds_read_tr(blk + rb->v[sd][ct & 1], (ct >> 1) * 128 + ks * 16 * kRowBytes);
   }
   __device__ __forceinline__ void start() {
@@ -454,13 +455,13 @@ template <> struct VStream<Bf16Kv> {
   }
 };
 
-template <> struct VStream<E4m3Kv> {
+template <int F> struct VStream<E4m3Kv, F> {
   static constexpr int DV = 4;  // reads in flight
   const uint8_t* blk;
   const ReadBases8* rb;
   i32x2 raw[DV];
   __device__ __forceinline__ i32x2 rd(int t) const {
-    const int ks = t >> 3, ct = t & 7;
+    const int ks = (t >> 3) ^ F, ct = t & 7;
     return lds_read_tr8(blk + rb->v[ct & 1], (ct >> 1) * 64 + ks * 16 * kRowBytes8);
   }
   __device__ __forceinline__ void start() {
@@ -494,13 +495,13 @@ template <> struct KStream<NopeKv> {
   }
 };
 
-template <> struct VStream<NopeKv> {
+template <int F> struct VStream<NopeKv, F> {
   static constexpr int DV = 4;  // read pairs in flight
   const uint8_t* blk;
   const ReadBasesN* rb;
   bf16x4 b0[DV], b1[DV];
   __device__ __forceinline__ bf16x4 rd(int t, int sd) const {
-    const int ks = t >> 3, ct = t & 7;
+    const int ks = (t >> 3) ^ F, ct = t & 7;
     return lds_read_tr(blk + rb->v[sd][ct & 3], (ct >> 2) * 256 + ks * 16 * kNopeRowBytes);
   }
   __device__ __forceinline__ void start() {
@@ -579,15 +580,23 @@ __device__ __forceinline__ void store_partial(f32x4* xs, const f32x16& s) {
 // the number of leading rows of block i this lane's query row may see; with a draft
 // tree, rows from `drow0` on are draft rows (row drow0 + u is draft u), seen only
 // where bit u of `tm` is set (drow0 >= 32 when the block holds no draft row).
-template <bool HAS_NEXT, class Kv>
+//
+// Both waves of a pair hold the full scores, but each computes the weights of one
+// k-step of P only (C = wave % 2: kv rows 16 C .. 16 C + 15 in accumulator order)
+// and hands them to the other through the other's S^T slot, which it has finished
+// reading; the barrier after the S^T MFMAs publishes them.  Its own k-step is the
+// first of its P V MFMAs, so the other's arrives under them.  Each wave's weight
+// sums cover its k-step; the piece's epilogue adds the pair's.
+template <bool HAS_NEXT, class Kv, int C>
 __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk_next,
                                           const typename Kv::Bases& rb, const bf16x8* qreg,
-                                          f32x16& s_own, f32x4* own, const f32x4* partner,
+                                          f32x16& s_own, f32x4* own, f32x4* partner,
                                           WaveState& ws, int lim, int drow0, uint64_t tm,
                                           float scale_log2, const CopyJob& job,
                                           const typename Kv::Offsets& so) {
   const int lane = threadIdx.x & 63;
   constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
+  static_assert(Kv::kQSteps >= 13, "the softmax step takes S^T slots 0..12");
 
   f32x4 pr[4];
 #pragma unroll
@@ -598,9 +607,9 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
 
   f32x16 x;
   f32x16 n0 = {};
-  float m_use = 0.0f, psum = 0.0f;
-  bf16x8 pa[2];
-  VStream<Kv> vst{blk, &rb};
+  float m_use = 0.0f, psum = 0.0f, mloc = 0.0f;
+  bf16x8 p_own, p_other;  // P for k-step C (computed here) and k-step 1 - C (received)
+  VStream<Kv, C> vst{blk, &rb};
 
   // ---- S^T of block i + 1 on the MFMA pipe, the softmax step of block i in between
 #pragma unroll
@@ -631,7 +640,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
     } else if (kk == 4) {
       // row max (a query row's 32 scores sit in lanes l and l + 32), in the log2
       // domain: scaling by a positive factor commutes with the max, rounding included
-      float mloc = x[0];
+      mloc = x[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
       mloc = pair32_max(mloc) * scale_log2;
@@ -639,11 +648,12 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
       if (ws.m_ref == -INFINITY) ws.m_ref = mloc;  // a row's first visible block sets it
       m_use = (ws.m_ref == -INFINITY) ? 0.0f : ws.m_ref;
     } else if (kk == 6 || kk == 8) {
-      const int i0 = kk == 6 ? 0 : 8;
+      // this wave's k-step: S^T registers 8 C .. 8 C + 7
+      const int i0 = 8 * C + (kk == 6 ? 0 : 4);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i0 + i] = __builtin_amdgcn_exp2f(fmaf(x[i0 + i], scale_log2, -m_use));
-        psum += x[i0 + i];
+      for (int i = i0; i < i0 + 4; ++i) {
+        x[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -m_use));
+        psum += x[i];
       }
     } else if (kk == 10) {
       // P as the A operand of O = P V: for k-step ks lane holds query row lane % 32 and
@@ -654,31 +664,35 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
       // than up to bf16 rounding.
       ws.l_run += psum;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) pa[ks][k] = static_cast<__bf16>(x[8 * ks + k]);
+      for (int k = 0; k < 8; ++k) p_own[k] = static_cast<__bf16>(x[8 * C + k]);
+      // to the other wave: into its S^T slot, whose reads (above) this wave has issued
+      // first, and LDS serves a wave's accesses in order
+      *reinterpret_cast<bf16x8*>(partner + lane) = p_own;
       // sum of the rounded weights, two at a time (products with 1 are exact)
       const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
       float pbf = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int k = 0; k < 8; k += 2)
-          pbf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pa[ks][k], pa[ks][k + 1]}, ones, pbf, false);
+      for (int k = 0; k < 8; k += 2)
+        pbf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p_own[k], p_own[k + 1]}, ones, pbf, false);
       ws.l_bf += pbf;
     } else if (kk == 12) {
-      vst.start();  // the first V operands of block i
+      vst.start();  // the first V operands of block i (this wave's k-step)
     }
-    if (HAS_NEXT && kk == Kv::kQSteps - 1) __syncthreads();  // block i's halves are read
+    if (kk == Kv::kQSteps - 1) {
+      // the weights are in every slot, and (when HAS_NEXT) block i's halves are read
+      __syncthreads();
+      p_other = *reinterpret_cast<const bf16x8*>(own + lane);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- O += P V, V = this wave's 256 c_kv columns of block i, read transposed
+  // ---- O += P V, V = this wave's 256 c_kv columns of block i, read transposed; this
+  // wave's k-step first
 #pragma unroll
   for (int t = 0; t < NPV; ++t) {
-    ws.acc[t & 7] = mfma32(pa[t >> 3], vst.next(t), ws.acc[t & 7]);
+    ws.acc[t & 7] = mfma32(t < 8 ? p_own : p_other, vst.next(t), ws.acc[t & 7]);
     if constexpr (HAS_NEXT) {
-      if (t == 8) {  // block i + 1's half is complete
+      if (t == 8) {  // block i + 1's half is complete; the received weights are read
         store_partial(own, n0);
         s_own = n0;
       }
@@ -793,7 +807,7 @@ __device__ __forceinline__ void wait_copy_sets(int sets) {
 // walked as 32-row blocks through a ring of kStagesN slots: while block i is scored
 // (softmax, P V) and block i + 1's S^T is computed, blocks i + 2 .. i + kStagesN - 1
 // are in flight.
-template <class Kv>
+template <class Kv, int C>
 __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32x4* xbuf, int b,
                                           int L, int mt, int lo, int hi, bool whole, int slot) {
   constexpr int S = Kv::kStagesN;
@@ -848,7 +862,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   wait_vmem_all();  // queries and page ids are in before any block copy is counted
 
   f32x4* own = xbuf + wave * 4 * 64;  // this wave's S^T half (4 x 64 lanes x f32x4)
-  const f32x4* partner = xbuf + (wave ^ 1) * 4 * 64;
+  f32x4* partner = xbuf + (wave ^ 1) * 4 * 64;
   auto lim_of = [&](int i) { return n_vis - (lo + (i >> 1)) * kPage - (i & 1) * kKvBlock; };
   // draft tree: this lane's ancestor bits (bits above its own draft ignored, its own
   // bit always set) and the block row where draft 0 sits
@@ -914,7 +928,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
         else
           Kv::stage(src_new, ring_slot<Kv>(ring, i + AHEAD), valid, so);
       }
-      pipe_step<true, Kv>(ring_slot<Kv>(ring, i), ring_slot<Kv>(ring, i + 1), rb, qreg, s_own,
+      pipe_step<true, Kv, C>(ring_slot<Kv>(ring, i), ring_slot<Kv>(ring, i + 1), rb, qreg, s_own,
                           own, partner, ws, lim_of(i), drow_of(i), tm, a.scale_log2, job, so);
 #pragma unroll
       for (int j = 0; j + 1 < AHEAD; ++j) srcs[j] = srcs[j + 1];
@@ -922,7 +936,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     }
     if (i < nb) {  // the last block (already in LDS): nothing left to score ahead or copy
       __syncthreads();
-      pipe_step<false, Kv>(ring_slot<Kv>(ring, i), nullptr, rb, qreg, s_own, own, partner, ws,
+      pipe_step<false, Kv, C>(ring_slot<Kv>(ring, i), nullptr, rb, qreg, s_own, own, partner, ws,
                            lim_of(i), drow_of(i), tm, a.scale_log2, CopyJob{}, so);
     }
     // a row whose scores outgrew its reference by more than the lazy bound forces a
@@ -939,7 +953,16 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     if (!redo) break;
   }
 
-  write_rows(a, ws, pair32_sum(ws.l_run), pair32_sum(ws.l_bf), b, m_slice, p * kRowsPerWave, c,
+  // the pair's weight sums: each wave summed the weights of its own k-step of P.  Both
+  // waves add them in the same order (the C = 0 wave's first), so both normalise their
+  // columns by the same sums.
+  f32x2* sums = reinterpret_cast<f32x2*>(xbuf);  // free: every wave is past the last use
+  sums[wave * 64 + lane] = f32x2{ws.l_run, ws.l_bf};
+  __syncthreads();
+  const f32x2 other = sums[(wave ^ 1) * 64 + lane];
+  const float l_run = C == 0 ? ws.l_run + other[0] : other[0] + ws.l_run;
+  const float l_bf = C == 0 ? ws.l_bf + other[1] : other[1] + ws.l_bf;
+  write_rows(a, ws, pair32_sum(l_run), pair32_sum(l_bf), b, m_slice, p * kRowsPerWave, c,
              whole, slot);
 }
 
@@ -1325,10 +1348,17 @@ splitkv_kernel(SplitArgs a) {
       const int plo = (int)((p0 > pb0 ? p0 : pb0) - pb0);
       const int phi = (int)((p1 < pb1 ? p1 : pb1) - pb0);
       const bool whole = plo == 0 && phi == pb1 - pb0;
-      run_piece<Kv>(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
-                    __builtin_amdgcn_readfirstlane(Lb), mt,
-                    __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi),
-                    whole, (b + g) * a.n_mt + mt);
+      // the two waves of a pair run the two k-step halves of P (wave-uniform branch)
+      if ((threadIdx.x >> 6) & 1)
+        run_piece<Kv, 1>(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
+                         __builtin_amdgcn_readfirstlane(Lb), mt,
+                         __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi),
+                         whole, (b + g) * a.n_mt + mt);
+      else
+        run_piece<Kv, 0>(a, ring, xbuf, __builtin_amdgcn_readfirstlane(b),
+                         __builtin_amdgcn_readfirstlane(Lb), mt,
+                         __builtin_amdgcn_readfirstlane(plo), __builtin_amdgcn_readfirstlane(phi),
+                         whole, (b + g) * a.n_mt + mt);
       if (a.arrive && !whole) {
         // single pass: every wave's partial stores have reached L2 before the barrier;
         // one release fence then writes the XCD's L2 back (it covers all four waves)
