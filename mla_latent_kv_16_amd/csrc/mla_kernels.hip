@@ -33,18 +33,24 @@ namespace mla {
 // A row's exp2 reference m_ref is the max of its first visible block and then stays
 // fixed while the piece is walked, so p = exp2(s - m_ref) needs no running rescale
 // of O inside the loop as long as later scores stay below m_ref + kLazyRescale
-// (p < 2^32, far inside the range of bf16 P and of the fp32 sums).  Every block
-// also tracks the row's true max; if any row of the workgroup broke the bound, the
-// piece is walked a second time with m_ref set to that max, where no score can
-// exceed it.  The final normalisation uses the same m_ref as the sums, so the
-// result does not depend on which reference was used.
+// (p < 2^32, far inside the range of bf16 P and of the fp32 sums).  Only blocks
+// where some row still lacks a reference take the row max; elsewhere each wave
+// bounds its weights by their per-block sum.  If any weight may have broken the
+// bound, the piece is walked again taking every block's max (which, with the
+// first block's reference again, usually breaks the same way but finds the true
+// maxima), and if need be a third time with m_ref set to those maxima, where no
+// score can exceed it.  The final normalisation uses the same m_ref as the sums, so
+// the result does not depend on which reference was used.
 constexpr float kLazyRescale = 32.0f;
+constexpr float kLazyWeight = 4294967296.0f;  // 2^kLazyRescale
 constexpr float kLn2 = 0.69314718055994531f;
 
 struct WaveState {
   f32x16 acc[kColTilesPerWave];  // O: column 256 c + 32 ct + lane % 32, rows acc_row(lane, i)
   float m_ref;                   // exp2 reference (log2 domain) of query row lane % 32
-  float m_seen;                  // max score of that row so far
+  float m_seen;                  // max score of that row over the blocks whose max was taken
+  float p_hi;                    // largest per-block sum of this lane's weights (a bound on
+                                 // each weight, for blocks whose max was not taken)
   float l_run;                   // this lane's share of that row's exp2 sum (gives the LSE)
   float l_bf;                    // the same sum over the bf16-rounded P that enters P V
 };
@@ -306,6 +312,7 @@ __device__ __forceinline__ ReadBasesN read_bases_nope(int c) {
 // in registers after the LDS read.
 struct Bf16Kv {
   static constexpr int kQSteps = kQStepsPerWave;  // MFMA k-steps per wave
+  static constexpr bool kLazyMax = true;          // row max only where a reference is due
   static constexpr bool kRopeQ = true;            // queries have a q_rope part
   static constexpr int kStagesN = kStages;        // ring slots
   static constexpr int kSlot = kStageBytes;       // bytes per slot
@@ -332,6 +339,7 @@ struct Bf16Kv {
 
 struct E4m3Kv {
   static constexpr int kQSteps = kQStepsPerWave;
+  static constexpr bool kLazyMax = false;  // measured slower with the widening VALU
   static constexpr bool kRopeQ = true;
   static constexpr int kStagesN = kStages8;
   static constexpr int kSlot = kSlotBytes8;
@@ -355,6 +363,7 @@ struct E4m3Kv {
 
 struct NopeKv {
   static constexpr int kQSteps = kNopeQSteps;
+  static constexpr bool kLazyMax = true;
   static constexpr bool kRopeQ = false;
   static constexpr int kStagesN = kStages;
   static constexpr int kSlot = kNopeBlockBytes;
@@ -593,11 +602,13 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
                                           f32x16& s_own, f32x4* own, f32x4* partner,
                                           WaveState& ws, int lim, int drow0, uint64_t tm,
                                           float scale_log2, const CopyJob& job,
-                                          const typename Kv::Offsets& so) {
+                                          const typename Kv::Offsets& so, bool full) {
   const int lane = threadIdx.x & 63;
   constexpr int NPV = 2 * kColTilesPerWave;  // 16 MFMAs: 2 k-steps x 8 column tiles
   static_assert(Kv::kQSteps >= 13, "the softmax step takes S^T slots 0..12");
 
+  // `full` (wave-uniform): this block takes the row max, which needs all 32 scores
+  // of a row; otherwise only this wave's k-step (S^T registers 8 C .. 8 C + 7) is summed
   f32x4 pr[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) pr[j] = partner[j * 64 + lane];
@@ -623,9 +634,15 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
       // full scores: own half + partner half (the same sum on both waves of the pair,
       // fp32 addition being commutative); the log2-domain scale is applied below
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 2 * C; j < 2 * C + 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[4 * j + e] = s_own[4 * j + e] + pr[j][e];
+      if (full) {
+#pragma unroll
+        for (int j = 2 - 2 * C; j < 4 - 2 * C; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * j + e] = s_own[4 * j + e] + pr[j][e];
+      }
     } else if (kk == 2) {
       if (__builtin_amdgcn_ballot_w64(lim < kKvBlock || drow0 < kKvBlock)) {
 #pragma unroll
@@ -638,14 +655,16 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
         }
       }
     } else if (kk == 4) {
-      // row max (a query row's 32 scores sit in lanes l and l + 32), in the log2
-      // domain: scaling by a positive factor commutes with the max, rounding included
-      mloc = x[0];
+      if (full) {
+        // row max (a query row's 32 scores sit in lanes l and l + 32), in the log2
+        // domain: scaling by a positive factor commutes with the max, rounding included
+        mloc = x[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
-      mloc = pair32_max(mloc) * scale_log2;
-      ws.m_seen = fmaxf(ws.m_seen, mloc);
-      if (ws.m_ref == -INFINITY) ws.m_ref = mloc;  // a row's first visible block sets it
+        for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+        mloc = pair32_max(mloc) * scale_log2;
+        ws.m_seen = fmaxf(ws.m_seen, mloc);
+        if (ws.m_ref == -INFINITY) ws.m_ref = mloc;  // a row's first visible block sets it
+      }
       m_use = (ws.m_ref == -INFINITY) ? 0.0f : ws.m_ref;
     } else if (kk == 6 || kk == 8) {
       // this wave's k-step: S^T registers 8 C .. 8 C + 7
@@ -663,6 +682,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* blk, const uint8_t* blk
       // row dominated by one key returns that key's c_kv up to fp32 rounding rather
       // than up to bf16 rounding.
       ws.l_run += psum;
+      if (!full) ws.p_hi = fmaxf(ws.p_hi, psum);  // every weight is <= its sum
 #pragma unroll
       for (int k = 0; k < 8; ++k) p_own[k] = static_cast<__bf16>(x[8 * C + k]);
       // to the other wave: into its S^T slot, whose reads (above) this wave has issued
@@ -881,13 +901,21 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
   // only adds to that count)
   const int sets_after = min(nb, AHEAD) - 2;
 
-  // At most two passes: the second (rare) one starts from the rows' true maxima.
-  for (int pass = 0; pass < 2; ++pass) {
+  // At most three passes (rare): pass 0 takes a block's row max only where a row
+  // lacks its reference, pass 1 takes every block's, pass 2 starts from the true
+  // maxima that pass 1 found.  Formats without the lazy max start at pass 1.
+  for (int pass = Kv::kLazyMax ? 0 : 1; pass < 3; ++pass) {
 #pragma unroll
     for (int ct = 0; ct < kColTilesPerWave; ++ct) ws.acc[ct] = f32x16{};
-    ws.m_ref = pass == 0 ? -INFINITY : ws.m_seen;
+    ws.m_ref = pass < 2 ? -INFINITY : ws.m_seen;
     ws.l_run = 0.0f;
     ws.l_bf = 0.0f;
+    ws.p_hi = 0.0f;
+    // the row max is due where a row has no reference yet and sees rows of the block
+    auto full_max = [&](int i) {
+      return !Kv::kLazyMax || pass > 0 ||
+             __builtin_amdgcn_ballot_w64(ws.m_ref == -INFINITY && lim_of(i) > 0);
+    };
     // Block j is copied into ring slot j % S during iteration j - AHEAD (the slot's
     // previous block, j - S, was finished in iteration j - S), its S^T halves are
     // computed in iteration j - 1 and its softmax and P V run in iteration j.  A
@@ -928,20 +956,24 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
         else
           Kv::stage(src_new, ring_slot<Kv>(ring, i + AHEAD), valid, so);
       }
-      pipe_step<true, Kv, C>(ring_slot<Kv>(ring, i), ring_slot<Kv>(ring, i + 1), rb, qreg, s_own,
-                          own, partner, ws, lim_of(i), drow_of(i), tm, a.scale_log2, job, so);
+      pipe_step<true, Kv, C>(ring_slot<Kv>(ring, i), ring_slot<Kv>(ring, i + 1), rb, qreg,
+                             s_own, own, partner, ws, lim_of(i), drow_of(i), tm, a.scale_log2,
+                             job, so, full_max(i));
 #pragma unroll
       for (int j = 0; j + 1 < AHEAD; ++j) srcs[j] = srcs[j + 1];
       srcs[AHEAD - 1] = src_new;
     }
     if (i < nb) {  // the last block (already in LDS): nothing left to score ahead or copy
       __syncthreads();
-      pipe_step<false, Kv, C>(ring_slot<Kv>(ring, i), nullptr, rb, qreg, s_own, own, partner, ws,
-                           lim_of(i), drow_of(i), tm, a.scale_log2, CopyJob{}, so);
+      pipe_step<false, Kv, C>(ring_slot<Kv>(ring, i), nullptr, rb, qreg, s_own, own, partner,
+                              ws, lim_of(i), drow_of(i), tm, a.scale_log2, CopyJob{}, so,
+                              full_max(i));
     }
-    // a row whose scores outgrew its reference by more than the lazy bound forces a
-    // second pass for the whole workgroup; the flag lives in the exchange buffer
-    const bool broke = ws.m_ref != -INFINITY && ws.m_seen > ws.m_ref + kLazyRescale;
+    // a row whose scores outgrew its reference by more than the lazy bound (or a
+    // weight sum past it, in a block without the max) forces another pass for the
+    // whole workgroup; the flag lives in the exchange buffer
+    const bool broke = (ws.m_ref != -INFINITY && ws.m_seen > ws.m_ref + kLazyRescale) ||
+                       ws.p_hi > kLazyWeight;
     int* redo_flag = reinterpret_cast<int*>(xbuf);
     __syncthreads();  // every wave is done with the ring and the exchange buffer
     if (threadIdx.x == 0) *redo_flag = 0;
