@@ -126,8 +126,9 @@ def measured_peaks(torch, dev):
 
 
 def stored_traffic(config, kv):
-    """HBM bytes per split-KV launch from profiles/traffic_<config>[_e4m3].json, if
-    the counters were taken on the current kernel sources."""
+    """HBM bytes per split-KV launch from profiles/traffic_<config>[_e4m3|_nope].json,
+    if the counters were taken on the current kernel sources (kv: bf16, e4m3 or nope,
+    the pool format they were taken with)."""
     from mla_latent_kv_16_amd.profiling import kernel_hash
     tag = config if kv == "bf16" else f"{config}_{kv}"
     path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
@@ -369,7 +370,7 @@ def main():
     # the dominant kernel's average launch duration: per-launch events on its stream
     hbm_achieved = work["bytes"] / (split_avg * 1e-3) / 1e9
     mfma_achieved = work["flops"] / (split_avg * 1e-3) / 1e12
-    traffic = stored_traffic(args.config, args.kv)
+    traffic = stored_traffic(args.config, "nope" if args.nope else args.kv)
     # the bound is the roof the step's arithmetic intensity meets first
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     mfma_bound = work["flops"] / work["bytes"] > ridge
