@@ -1,0 +1,95 @@
+"""Host logic of the measurement tooling (no GPU): rocprofv3 CSV summaries, the
+counter-calibrated traffic per launch, the bench table, and bench.py's lookup of
+stored traffic by workload and pool format."""
+import csv
+import importlib.util
+import json
+import os
+
+import pytest
+
+from mla_latent_kv_16_amd import profiling as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _write_counters(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for k, c, v in rows:
+            w.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_kernel_hash_is_stable_hex():
+    h = P.kernel_hash()
+    assert len(h) == 16 and int(h, 16) >= 0
+    assert P.kernel_hash() == h
+
+
+def test_traffic_scales_each_counter_by_the_copy_probe(tmp_path):
+    kib = P.COPY_PROBE_BYTES / 1024
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    # the copy probe reads half its bytes on FETCH_SIZE and all of them on WRITE_SIZE;
+    # a small copy kernel of the same name is ignored (only the largest dispatches count)
+    _write_counters(fetch, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", kib / 2),
+                            ("__amd_rocclr_copyBuffer", "FETCH_SIZE", kib / 2),
+                            ("__amd_rocclr_copyBuffer", "FETCH_SIZE", 3.0),
+                            ("void mla::splitkv_kernel<mla::Bf16Kv>(mla::SplitArgs)",
+                             "FETCH_SIZE", 1000.0),
+                            ("void mla::splitkv_kernel<mla::Bf16Kv>(mla::SplitArgs)",
+                             "FETCH_SIZE", 3000.0),
+                            ("mla::combine_kernel(mla::CombineArgs)", "FETCH_SIZE", 50.0)])
+    _write_counters(write, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", kib),
+                            ("void mla::splitkv_kernel<mla::Bf16Kv>(mla::SplitArgs)",
+                             "WRITE_SIZE", 400.0),
+                            ("mla::combine_kernel(mla::CombineArgs)", "WRITE_SIZE", 8.0)])
+    r = P.traffic(str(fetch), str(write), "spec4", "cmd")
+    assert r["fetch_scale"] == pytest.approx(2.0) and r["write_scale"] == pytest.approx(1.0)
+    assert r["split_fetch_bytes"] == pytest.approx(2000.0 * 1024 * 2.0)
+    assert r["split_write_bytes"] == pytest.approx(400.0 * 1024)
+    assert r["combine_fetch_bytes"] == pytest.approx(50.0 * 1024 * 2.0)
+    assert r["kernel_hash"] == P.kernel_hash()
+
+
+def test_bench_table_renders_a_row(tmp_path):
+    rec = {"value": 3853.5, "us_per_step": 78.4, "us_per_step_graph_replay": 83.1,
+           "kv_frac_of_hbm_peak": 0.4817, "split_pass_us": 69.3,
+           "split_kernel_us_back_to_back": 66.1, "single_pass_us_per_step": None,
+           "config": {"workload": "spec4", "latent": "512+64 e4m3, per-tensor scale"},
+           "roofline": {"bound": "hbm", "achieved": 4369.2, "unit": "GB/s", "frac": 0.5462,
+                        "frac_of_measured_peak": 0.88},
+           "cpu_baseline": None}
+    src = tmp_path / "b.jsonl"
+    src.write_text("noise\n" + json.dumps(rec) + "\n")
+    table = P.bench_table(str(src))
+    rows = table.splitlines()
+    assert len(rows) == 3
+    cells = [c.strip() for c in rows[2].strip("|").split("|")]
+    assert cells[:3] == ["spec4", "e4m3", "78.4"]
+    assert cells[7] == "—" and cells[-1] == "—"
+    assert "4369.2 GB/s (54.6%)" in rows[2]
+
+
+def test_stored_traffic_follows_the_pool_format():
+    """bench.py reports stored HBM traffic only for the pool format and kernel sources
+    the counters were taken on: NoPE pools have no counters of their own, so they get
+    none (not the bf16 pool's)."""
+    b = _bench()
+    path = os.path.join(ROOT, "profiles", "traffic_spec4.json")
+    with open(path) as f:
+        rec = json.load(f)
+    got = b.stored_traffic("spec4", "bf16")
+    if rec["kernel_hash"] == P.kernel_hash():
+        assert got == int(rec["split_fetch_bytes"] + rec["split_write_bytes"])
+    else:
+        assert got is None
+    assert b.stored_traffic("spec4", "nope") is None
+    assert b.stored_traffic("no-such-workload", "bf16") is None
