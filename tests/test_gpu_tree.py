@@ -99,6 +99,11 @@ TREES = [
     ("random-odd", dict(seed=414, B=2, Sq=37, H=3, lens=("uniform", 100, 400)), "random", 0),
     ("drafts-cross-page", dict(seed=415, B=2, Sq=20, H=16, lens=("fixed", 64 * 7 + 10)), "random", 2),
     ("drafts-only", dict(seed=416, B=2, Sq=12, H=16, lens=("fixed", 12)), "random", 0),
+    # three one-page partitions, the last holding the 64 drafts alone: under a star tree
+    # drafts 32..63 see nothing in that piece's first block, so their exp2 reference is
+    # set by its second block, while drafts 0..31 already have theirs
+    ("star-drafts-own-partition", dict(seed=417, B=1, Sq=64, H=2, lens=("fixed", 64 * 3)),
+     "star", 3),
 ]
 
 
