@@ -65,6 +65,28 @@ def algorithmic_work(w):
     return dict(kv_bytes=kv, bytes=kv + q + out + bt, flops=flops, pages=pages)
 
 
+def host_cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None where unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_name():
+    """The BLAS numpy was built against (name and version), or None."""
+    import numpy as np
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{blas.get('name')} {blas.get('version')}"
+    except Exception:
+        return None
+
+
 def cpu_baseline(w, budget_s=12.0):
     """fp64 oracle on whole requests (cycling through the batch) until ~budget_s has
     passed; KV bytes of the requests done over the wall time, in GB/s."""
@@ -91,6 +113,7 @@ def cpu_baseline(w, budget_s=12.0):
             break
     dt = time.perf_counter() - t0
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": host_cpu_model(), "blas": blas_name(),
             "sample": f"{done} request passes (cycling over the {w.B} requests of the same "
                       f"workload), fp64 numpy, {dt:.1f} s wall",
             "seconds_per_step_extrapolated": dt * w.B / done}

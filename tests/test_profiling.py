@@ -93,3 +93,10 @@ def test_stored_traffic_follows_the_pool_format():
         assert got is None
     assert b.stored_traffic("spec4", "nope") is None
     assert b.stored_traffic("no-such-workload", "bf16") is None
+
+
+def test_cpu_baseline_names_its_host():
+    b = _bench()
+    model, blas = b.host_cpu_model(), b.blas_name()
+    assert model is None or (isinstance(model, str) and model)
+    assert blas is None or (isinstance(blas, str) and blas)
