@@ -81,9 +81,11 @@ const char* mla_status_string(int status);
 /*
  * Number of KV partitions ("splits") the decode entry points use when called with
  * num_partitions = 0, on the current HIP device.  Each partition is a contiguous
- * run of pages of the batch's concatenated page list; partitions are sized so the
- * grid covers the device's compute units once.  A result of 1 means no split and
- * no combine pass.  Returns a status; *num_partitions receives the count.
+ * run of pages of the batch's concatenated page list.  The count comes from a cost
+ * model measured on MI355X: at most one (partition x M-tile) workgroup per compute
+ * unit, and fewer where the partial results a split writes and merges cost more than
+ * its shorter page walks save (short contexts).  A result of 1 means no split and no
+ * combine pass.  Returns a status; *num_partitions receives the count.
  */
 int mla_decode_auto_partitions(int B, int Sq, int H, int max_pages_per_seq,
                                int* num_partitions);

@@ -51,15 +51,39 @@ int geometry(int B, int Sq, int H, int max_pages, Geometry* g) {
   return MLA_OK;
 }
 
-// Default partition count: enough (partition x M-tile) workgroups to cover the
-// compute units once, never more partitions than a few pages each can justify.
+// Default partition count, from a cost model of one decode measured on MI355X: a
+// workgroup walks its partition at about 2.8 us per page (two 32-row blocks), a
+// split writes and re-reads its partial results (min(M, 64) rows x 513 floats per
+// piece) at about 0.44 us per MB, and adds one merge launch (about 4 us).  Long
+// contexts take the most partitions (the walk dominates); short ones trade
+// parallelism against partial traffic.  Candidates are multiples of B, up to one
+// (partition x M-tile) workgroup per compute unit, so that equal requests split
+// evenly; below four pages per partition a candidate must also divide the page count,
+// since a partition that straddles two requests walks and writes two pieces.  The
+// page count is the block table's capacity, an upper bound of the real one.
 int auto_partitions(const Geometry& g, int B, int max_pages, int cus) {
-  const int64_t total_pages = (int64_t)B * max_pages;  // upper bound of the real total
-  int64_t G = cus / g.n_mt;
-  const int64_t by_pages = (total_pages + 3) / 4;       // at least ~4 pages per partition
-  if (G > by_pages) G = by_pages;
-  if (G < 1) G = 1;
-  return (int)G;
+  constexpr double kUsPerPage = 2.8, kUsPerPartialMB = 0.44, kUsMerge = 4.0;
+  const int64_t pages = (int64_t)B * max_pages;
+  int64_t gmax = cus / g.n_mt;
+  if (gmax > pages) gmax = pages;
+  if (gmax < 1) gmax = 1;
+  if (B > gmax) {  // fewer partitions than requests: at least about four pages each
+    const int64_t by_pages = (pages + 3) / 4;
+    return (int)(by_pages < gmax ? by_pages : gmax);
+  }
+  const double piece_mb = (double)g.n_mt * g.slot_rows * (kNope + 1) * 4 * 1e-6;
+  int64_t best = 1;
+  double best_us = (double)pages * kUsPerPage;
+  for (int64_t G = B; G <= gmax; G += B) {
+    if (G == 1 || (pages < 4 * G && pages % G != 0)) continue;
+    const double us = (double)pages / (double)G * kUsPerPage +
+                      (double)G * piece_mb * kUsPerPartialMB + kUsMerge;
+    if (us < best_us) {
+      best_us = us;
+      best = G;
+    }
+  }
+  return (int)best;
 }
 
 int resolve_partitions(const Geometry& g, int B, int max_pages, int requested, int* G) {

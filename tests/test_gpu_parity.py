@@ -244,6 +244,22 @@ def test_maximum_batch(parts, single):
     check(O, lse, *oracle(w), f"B=1024 parts={parts} single={single}")
 
 
+# default partition counts (256 CUs): the long-context decode shapes take one
+# (partition x M-tile) workgroup per CU, prefill none, and short contexts the count
+# the cost model picks (each measured faster than the old four-pages floor, or equal)
+AUTO_G = [((1, 1, 16, 4), 4), ((4, 4, 16, 1025), 256), ((8, 8, 16, 2049), 128),
+          ((16, 16, 16, 3201), 64), ((64, 1, 128, 512), 128), ((1, 4096, 16, 1088), 1),
+          ((1, 4, 16, 16), 16), ((4, 4, 16, 16), 64), ((16, 1, 16, 32), 256),
+          ((4, 4, 16, 32), 64), ((4, 4, 16, 128), 128), ((300, 1, 16, 10), 256)]
+
+
+@pytest.mark.parametrize("shape,G", AUTO_G, ids=[str(a[0]) for a in AUTO_G])
+def test_default_partition_counts(shape, G):
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("counts are for a 256-CU device")
+    assert mla.auto_partitions(*shape) == G
+
+
 def test_batch_over_the_limit_is_rejected():
     w = make_workload("tiny", seed=141, B=1025, Sq=1, H=16, lens=("fixed", 64))
     with pytest.raises(mla.MLAError):
