@@ -80,18 +80,26 @@ def test_bench_table_renders_a_row(tmp_path):
 
 def test_stored_traffic_follows_the_pool_format():
     """bench.py reports stored HBM traffic only for the pool format and kernel sources
-    the counters were taken on: NoPE pools have no counters of their own, so they get
-    none (not the bf16 pool's)."""
+    the counters were taken on: a NoPE pool reads its own file (never the bf16 pool's),
+    and a format without counters gets none."""
     b = _bench()
-    path = os.path.join(ROOT, "profiles", "traffic_spec4.json")
-    with open(path) as f:
-        rec = json.load(f)
-    got = b.stored_traffic("spec4", "bf16")
-    if rec["kernel_hash"] == P.kernel_hash():
-        assert got == int(rec["split_fetch_bytes"] + rec["split_write_bytes"])
-    else:
-        assert got is None
-    assert b.stored_traffic("spec4", "nope") is None
+
+    def expect(tag):
+        path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
+        if not os.path.exists(path):
+            return None
+        with open(path) as f:
+            rec = json.load(f)
+        if rec["kernel_hash"] != P.kernel_hash():
+            return None
+        return int(rec["split_fetch_bytes"] + rec["split_write_bytes"])
+
+    assert b.stored_traffic("spec4", "bf16") == expect("spec4")
+    assert b.stored_traffic("spec4", "nope") == expect("spec4_nope")
+    if expect("spec4") is not None and expect("spec4_nope") is not None:
+        assert expect("spec4_nope") < expect("spec4")  # 1,024- against 1,152-byte rows
+    assert b.stored_traffic("spec4", "e4m3") == expect("spec4_e4m3")
+    assert b.stored_traffic("spec8", "e4m3") is None  # no counters taken for it
     assert b.stored_traffic("no-such-workload", "bf16") is None
 
 
