@@ -409,7 +409,8 @@ def main():
         key = "mfma_bf16_matmul_TFLOPs" if mfma_bound else "hbm_copy_GBps"
         roof["frac_of_measured_peak"] = round(roof["achieved"] / peaks[key], 4)
     log(f"step {ms_step * 1e3:.1f} us (split pass {split_avg * 1e3:.1f} us with per-launch events, "
-        f"p10 {np.percentile(split_ms, 10) * 1e3:.1f} p90 {np.percentile(split_ms, 90) * 1e3:.1f}; "
+        f"median {np.median(split_ms) * 1e3:.1f} p10 {np.percentile(split_ms, 10) * 1e3:.1f} "
+        f"p90 {np.percentile(split_ms, 90) * 1e3:.1f}; "
         f"{split_b2b * 1e3:.1f} us back to back); {value:.0f} GB/s of KV; split kernel "
         f"{hbm_achieved:.0f} GB/s, {mfma_achieved:.1f} TFLOP/s")
 
@@ -446,6 +447,7 @@ def main():
                    "kv_bytes": work["kv_bytes"], "tflops_per_step": work["flops"] / 1e12},
         "kv_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "split_pass_us": round(split_avg * 1e3, 2),
+        "split_pass_us_median": round(float(np.median(split_ms)) * 1e3, 2),
         "split_pass_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
                                   round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
         "split_kernel_us_back_to_back": round(split_b2b * 1e3, 2),
