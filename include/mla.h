@@ -37,10 +37,16 @@
  * - Errors are status codes, never exceptions.  Argument checks run on the host
  *   before anything is enqueued; on any error nothing is enqueued.
  * - Data the host cannot see (seq_lens and block_table contents) is checked by the
- *   kernels: a length outside [Sq, 64 * max_pages_per_seq] or a page id outside
- *   [0, num_pages) is clamped so that no access leaves the buffers, and a flag is
- *   raised in the workspace header; mla_read_error_flags() reports it.  Outputs of
- *   such a call are unspecified.
+ *   kernels on every call: a length outside [Sq, 64 * max_pages_per_seq] or a page
+ *   id outside [0, num_pages) is clamped so that no access leaves the buffers, and a
+ *   flag is raised in the workspace header; mla_read_error_flags() reports it.
+ *   Outputs of such a call are unspecified.  The clamp costs nothing on the fast
+ *   path, so it is always on; only the REPORT is optional.  In checked mode
+ *   (environment variable MLA_CHECK=1 when the call is made) every compute entry
+ *   point that takes a workspace also waits for its own work, moves the flags out
+ *   of the header and returns MLA_ERR_DEVICE_CHECK if any was raised.  Checked mode
+ *   synchronises the stream on every call (no graph capture, no overlap), so it is
+ *   for tests and debugging runs.
  * - Rows at or past L_b in a request's last page and block-table entries past
  *   ceil(L_b / 64) are never read; they may hold anything (NaN included).
  * - O and lse are written for every (b, t, h), and may not alias any input.
@@ -60,15 +66,18 @@ typedef enum {
   MLA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, non-positive size, NaN scale */
   MLA_ERR_UNSUPPORTED = -2,  /* page_size != 64, batch or grid beyond the library's limits */
   MLA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the size query returned */
-  MLA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_DEVICE_CHECK = -5  /* checked mode only: the kernels raised a data-fault flag */
 } mla_status_t;
+/* Every entry point returns its status as a plain int holding one of these values
+ * (an int has one size and calling convention in every C and C++ compiler, which an
+ * enum return type does not guarantee across them). */
 
 /* Device-side data faults reported through the workspace header. */
 #define MLA_FLAG_BAD_SEQ_LEN 1u  /* some seq_lens[b] < Sq or > 64 * max_pages_per_seq */
 #define MLA_FLAG_BAD_PAGE_ID 2u  /* some visible block_table entry outside [0, num_pages) */
 #define MLA_FLAG_MERGE_WAIT 4u   /* a single-pass merge gave up waiting (one second) for the
-                                    partials of its request: its outputs are unspecified and
-                                    the workspace must be zero-filled again before reuse */
+                                    partials of its request: its outputs are unspecified */
 
 #define MLA_PAGE_SIZE 64
 #define MLA_NOPE_DIM 512
@@ -85,7 +94,10 @@ const char* mla_status_string(int status);
  * model measured on MI355X: at most one (partition x M-tile) workgroup per compute
  * unit, and fewer where the partial results a split writes and merges cost more than
  * its shorter page walks save (short contexts).  A result of 1 means no split and no
- * combine pass.  Returns a status; *num_partitions receives the count.
+ * combine pass.  Returns a status; *num_partitions receives the count.  The model
+ * counts B * max_pages_per_seq pages, the block table's capacity: a caller whose
+ * table is much wider than its real contexts gets more partitions (and a larger
+ * workspace) than the real page count would pick, and can pass an explicit count.
  */
 int mla_decode_auto_partitions(int B, int Sq, int H, int max_pages_per_seq,
                                int* num_partitions);
@@ -98,6 +110,16 @@ int mla_decode_auto_partitions(int B, int Sq, int H, int max_pages_per_seq,
  */
 int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq,
                               int num_partitions, size_t* bytes);
+
+/*
+ * The same size for the automatic partition count of mla_decode (num_partitions =
+ * 0) and of mla_prefill_with_prefix, on the current device, as a plain value: 0
+ * where the sizes are invalid or unsupported (the compute call would reject them
+ * too) or the device cannot be queried.  A caller that passes its own
+ * num_partitions sizes the workspace with mla_decode_workspace_size instead.
+ */
+size_t mla_decode_workspace_bytes(int B, int Sq, int H, int max_pages_per_seq);
+size_t mla_prefill_workspace_bytes(int B, int Sq, int H, int max_pages_per_seq);
 
 /*
  * Speculative-verify / plain decode over the paged latent cache ("Faster kernels,
@@ -120,9 +142,8 @@ int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq,
  *   lse          fp32 [B, Sq, H]        natural-log log-sum-exp of the scaled scores
  *   workspace    device buffer of at least mla_decode_workspace_size() bytes,
  *                16-byte aligned, zero-filled before its first use (the error-flag
- *                header and the single-pass counters must start at zero; every
- *                call leaves the counters at zero again, so a workspace is zeroed
- *                once).
+ *                word in its 256-byte header must start at zero; everything past the
+ *                header is scratch that each call writes before it reads it).
  */
 int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
                int64_t num_pages, int page_size,
@@ -137,7 +158,10 @@ int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* k
  * them through counters in the workspace.  Same arguments, meaning and results (bit
  * for bit) as mla_decode.  On MI355X it is slower than the two launches: publishing
  * the partials across the eight XCDs' L2 caches costs more than the second launch
- * saves.  Calls that share a workspace must not overlap.
+ * saves.  Its arrival counters live in the workspace and are zeroed by a small
+ * kernel launched ahead of the decode on the same stream, so a workspace can serve
+ * single-pass and two-pass calls of any shapes in turn.  Calls that share a
+ * workspace must not overlap.
  */
 int mla_decode_single_pass(const uint16_t* q_nope, const uint16_t* q_rope,
                            const uint16_t* kv_pool, int64_t num_pages, int page_size,

@@ -33,5 +33,6 @@ from ._binding import (  # noqa: F401
     prefill_with_prefix,
     read_error_flags,
     status_string,
+    workspace_bytes,
     workspace_size,
 )

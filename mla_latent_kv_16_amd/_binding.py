@@ -20,6 +20,7 @@ MLA_ERR_INVALID_ARG = -1
 MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_WORKSPACE = -3
 MLA_ERR_HIP = -4
+MLA_ERR_DEVICE_CHECK = -5
 MLA_FLAG_BAD_SEQ_LEN = 1
 MLA_FLAG_BAD_PAGE_ID = 2
 PAGE_SIZE = 64
@@ -42,6 +43,8 @@ _SIGNATURES = {
     "mla_status_string": ([_i32], ctypes.c_char_p),
     "mla_decode_auto_partitions": ([_i32, _i32, _i32, _i32, ctypes.POINTER(_i32)], _i32),
     "mla_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
+    "mla_decode_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "mla_prefill_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "mla_decode": (_COMPUTE_ARGS, _i32),
     "mla_decode_splitkv": (_COMPUTE_ARGS, _i32),
     "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
@@ -121,6 +124,12 @@ def workspace_size(B: int, Sq: int, H: int, max_pages_per_seq: int, num_partitio
     _check(lib().mla_decode_workspace_size(B, Sq, H, max_pages_per_seq, num_partitions,
                                            ctypes.byref(out)), "mla_decode_workspace_size")
     return out.value
+
+
+def workspace_bytes(B: int, Sq: int, H: int, max_pages_per_seq: int, prefill: bool = False) -> int:
+    """Workspace bytes for the automatic partition count (0 = sizes rejected)."""
+    fn = lib().mla_prefill_workspace_bytes if prefill else lib().mla_decode_workspace_bytes
+    return int(fn(B, Sq, H, max_pages_per_seq))
 
 
 def _torch():

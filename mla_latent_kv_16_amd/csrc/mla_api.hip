@@ -5,6 +5,7 @@
 #include "mla_internal.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <mutex>
 
 namespace {
@@ -141,6 +142,35 @@ Layout carve(void* ws, const Geometry& g, int B, int G) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Waits for the stream, then moves the workspace header's flag word to *flags and
+// clears it.
+int take_flags(void* workspace, hipStream_t s, uint32_t* flags) {
+  if (hipStreamSynchronize(s) != hipSuccess) return MLA_ERR_HIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  const uint32_t zero = 0;
+  if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+    return MLA_ERR_HIP;
+  *flags = v;
+  return MLA_OK;
+}
+
+// Checked mode (environment MLA_CHECK=1): a compute call that enqueued its work also
+// waits for it and turns a raised data-fault flag into MLA_ERR_DEVICE_CHECK.  Off by
+// default, since waiting forces a synchronisation on every call.
+bool checked_mode() {
+  const char* v = getenv("MLA_CHECK");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+int finish(int st, void* workspace, hipStream_t s) {
+  if (st != MLA_OK || !checked_mode()) return st;
+  uint32_t flags = 0;
+  const int rd = take_flags(workspace, s, &flags);
+  if (rd != MLA_OK) return rd;
+  return flags ? MLA_ERR_DEVICE_CHECK : MLA_OK;
+}
+
 struct Call {
   Geometry geo;
   int G;
@@ -227,6 +257,11 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
       const int64_t per_wave = (rows + (int64_t)kWaves * cus - 1) / ((int64_t)kWaves * cus);
       a.comb_rows = (int)(per_wave < 1 ? 1 : per_wave);
     }
+    // The counters share the workspace with the partial results of calls of other
+    // shapes (whose partial slots may lie where this call's counters are), so they
+    // are zeroed before every single-pass launch rather than trusted to be zero.
+    if (launch_clear_words(c.lay.arrive, 2 * (int64_t)B * c.geo.n_mt, stream) != hipSuccess)
+      return MLA_ERR_HIP;
   }
   return launch_splitkv(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -274,8 +309,9 @@ int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_p
   st = enqueue_split(c, q_nope, q_rope, kv_pool, kv_format, kv_scale, num_pages, block_table,
                      max_pages_per_seq, seq_lens, tree_mask, B, Sq, H, softmax_scale, causal, O,
                      lse, single_pass, s, q_lens);
-  if (st != MLA_OK || single_pass) return st;
-  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
+  if (st == MLA_OK && !single_pass)
+    st = enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse, s);
+  return finish(st, workspace, s);
 }
 
 }  // namespace
@@ -289,6 +325,9 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: unsupported size or page size";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+    case MLA_ERR_DEVICE_CHECK:
+      return "MLA_ERR_DEVICE_CHECK: the kernels flagged a bad seq_lens or block_table entry "
+             "(checked mode)";
     default: return "unknown mla status";
   }
 }
@@ -314,6 +353,16 @@ int mla_decode_workspace_size(int B, int Sq, int H, int max_pages_per_seq, int n
   return MLA_OK;
 }
 
+size_t mla_decode_workspace_bytes(int B, int Sq, int H, int max_pages_per_seq) {
+  size_t bytes = 0;
+  return mla_decode_workspace_size(B, Sq, H, max_pages_per_seq, 0, &bytes) == MLA_OK ? bytes : 0;
+}
+
+size_t mla_prefill_workspace_bytes(int B, int Sq, int H, int max_pages_per_seq) {
+  // prefill runs the same passes with the same automatic partition count
+  return mla_decode_workspace_bytes(B, Sq, H, max_pages_per_seq);
+}
+
 int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
                        int64_t num_pages, int page_size, const int32_t* block_table,
                        int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
@@ -324,9 +373,11 @@ int mla_decode_splitkv(const uint16_t* q_nope, const uint16_t* q_rope, const uin
                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
-  return enqueue_split(c, q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
-                       lse, false, static_cast<hipStream_t>(stream));
+  return finish(enqueue_split(c, q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages,
+                              block_table, max_pages_per_seq, seq_lens, nullptr, B, Sq, H,
+                              softmax_scale, causal, O, lse, false,
+                              static_cast<hipStream_t>(stream)),
+                workspace, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_splitkv_placement(const uint16_t* q_nope, const uint16_t* q_rope,
@@ -343,9 +394,11 @@ int mla_decode_splitkv_placement(const uint16_t* q_nope, const uint16_t* q_rope,
   if (st != MLA_OK) return st;
   if (!wg_trace || (reinterpret_cast<uintptr_t>(wg_trace) & 3)) return MLA_ERR_INVALID_ARG;
   if (wg_trace_len < 3 * (int64_t)c.G * c.geo.n_mt) return MLA_ERR_INVALID_ARG;
-  return enqueue_split(c, q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
-                       lse, false, static_cast<hipStream_t>(stream), nullptr, wg_trace);
+  return finish(enqueue_split(c, q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages,
+                              block_table, max_pages_per_seq, seq_lens, nullptr, B, Sq, H,
+                              softmax_scale, causal, O, lse, false,
+                              static_cast<hipStream_t>(stream), nullptr, wg_trace),
+                workspace, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_combine(const int32_t* seq_lens, int max_pages_per_seq, int B, int Sq, int H,
@@ -361,8 +414,9 @@ int mla_decode_combine(const int32_t* seq_lens, int max_pages_per_seq, int B, in
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < workspace_bytes_for(c.geo, B, c.G)) return MLA_ERR_WORKSPACE;
   c.lay = carve(workspace, c.geo, B, c.G);
-  return enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse,
-                         static_cast<hipStream_t>(stream));
+  return finish(enqueue_combine(c, seq_lens, max_pages_per_seq, B, Sq, H, O, lse,
+                                static_cast<hipStream_t>(stream)),
+                workspace, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
@@ -409,9 +463,11 @@ int mla_decode_splitkv_e4m3(const uint16_t* q_nope, const uint16_t* q_rope,
                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
-  return enqueue_split(c, q_nope, q_rope, kv_pool, kFormatE4m3, kv_scale, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
-                       lse, false, static_cast<hipStream_t>(stream));
+  return finish(enqueue_split(c, q_nope, q_rope, kv_pool, kFormatE4m3, kv_scale, num_pages,
+                              block_table, max_pages_per_seq, seq_lens, nullptr, B, Sq, H,
+                              softmax_scale, causal, O, lse, false,
+                              static_cast<hipStream_t>(stream)),
+                workspace, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_e4m3(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* kv_pool,
@@ -483,9 +539,11 @@ int mla_decode_splitkv_nope(const uint16_t* q_nope, const uint16_t* kv_pool, int
                    seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
                    workspace_bytes, &c);
   if (st != MLA_OK) return st;
-  return enqueue_split(c, q_nope, q_nope, kv_pool, kFormatNope, 1.0f, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, nullptr, B, Sq, H, softmax_scale, causal, O,
-                       lse, false, static_cast<hipStream_t>(stream));
+  return finish(enqueue_split(c, q_nope, q_nope, kv_pool, kFormatNope, 1.0f, num_pages,
+                              block_table, max_pages_per_seq, seq_lens, nullptr, B, Sq, H,
+                              softmax_scale, causal, O, lse, false,
+                              static_cast<hipStream_t>(stream)),
+                workspace, static_cast<hipStream_t>(stream));
 }
 
 int mla_decode_varlen(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
@@ -526,7 +584,8 @@ static int append_call(const uint16_t* kv_new, void* kv_pool, int e4m3, float kv
   a.Sq = Sq;
   a.e4m3 = e4m3;
   a.inv_scale = e4m3 ? 1.0f / kv_scale : 1.0f;
-  return launch_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_append(a, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP, workspace, s);
 }
 
 int mla_kv_append(const uint16_t* kv_new, uint16_t* kv_pool, int64_t num_pages, int page_size,
@@ -569,15 +628,7 @@ int mla_project_o(const float* O, const uint16_t* w_uv, float* out, int B, int S
 
 int mla_read_error_flags(void* workspace, void* stream, uint32_t* flags) {
   if (!workspace || !flags) return MLA_ERR_INVALID_ARG;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipStreamSynchronize(s) != hipSuccess) return MLA_ERR_HIP;
-  uint32_t v = 0;
-  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
-  const uint32_t zero = 0;
-  if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
-    return MLA_ERR_HIP;
-  *flags = v;
-  return MLA_OK;
+  return take_flags(workspace, static_cast<hipStream_t>(stream), flags);
 }
 
 }  // extern "C"

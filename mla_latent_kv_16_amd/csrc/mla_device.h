@@ -150,22 +150,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Issued as inline asm so that the compiler does not tie later LDS reads of the
 // *other* ring slots to these copies (it would wait for every copy in flight);
 // completion is awaited explicitly with wait_vmem_all() before the barrier that
-// publishes a slot.  M0 is reserved to the compiler, which on gfx9 and later sets
-// it only for instructions these kernels do not use (LDS-DMA builtins, message
-// sends, indirect register indexing), so the asm may overwrite it.  A write of M0
-// needs one wait state before a global load with the LDS bit reads it.  The base
-// and the LDS address are passed through readfirstlane (as unsigned 32-bit halves)
-// so that they are scalar operands even where the compiler cannot prove them
-// uniform.
+// publishes a slot.  The LDS address travels in M0: the operand is bound to M0 with
+// a register constraint, so the compiler writes M0 itself and knows it is taken.  A
+// write of M0 needs one wait state before a global load with the LDS bit reads it
+// (the s_nop).  The base and the LDS address are passed through readfirstlane (as
+// unsigned 32-bit halves) so that they are scalar operands even where the compiler
+// cannot prove them uniform.
 __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
   const uint64_t p = reinterpret_cast<uint64_t>(sbase_in);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
   const void* sbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(lds)
+               : "v"(voff), "s"(sbase), "{m0}"(lds)
                : "memory");
 }
 

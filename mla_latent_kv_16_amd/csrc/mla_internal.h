@@ -88,5 +88,6 @@ hipError_t launch_project(const float* O, const uint16_t* w_uv, float* out, int 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t stream);
 
 }  // namespace mla

@@ -1443,6 +1443,22 @@ hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Zeroes n words: the single-pass arrival and merged-row counters, before each
+// single-pass launch (a kernel rather than a memset node, so that a captured graph
+// replays it like any other launch).
+__global__ void __launch_bounds__(256) clear_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t groups = (n + 255) / 256;
+  if (groups > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)groups), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.M;
   if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidValue;

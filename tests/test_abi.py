@@ -27,8 +27,9 @@ def test_library_exports_every_header_function():
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
         "mla_decode_splitkv_e4m3", "mla_decode_splitkv_placement", "mla_decode_tree",
         "mla_decode_tree_e4m3",
-        "mla_decode_varlen", "mla_decode_workspace_size", "mla_kv_append", "mla_kv_append_e4m3", "mla_prefill_with_prefix", "mla_read_error_flags",
-        "mla_status_string"])
+        "mla_decode_varlen", "mla_decode_workspace_bytes", "mla_decode_workspace_size",
+        "mla_kv_append", "mla_kv_append_e4m3", "mla_prefill_with_prefix",
+        "mla_prefill_workspace_bytes", "mla_read_error_flags", "mla_status_string"])
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -47,9 +48,33 @@ def test_header_compiles_as_c():
 
 
 def test_status_strings():
-    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, -5):
         assert mla.status_string(s)
+    assert "DEVICE_CHECK" in mla.status_string(-5)
     assert "unknown" in mla.status_string(12345)
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_workspace_bytes", "mla_prefill_workspace_bytes"])
+@pytest.mark.parametrize("args", [(0, 4, 16, 10), (2, 0, 16, 10), (2, 4, 0, 10), (2, 4, 16, 0),
+                                  (1025, 1, 16, 4), (1, 1 << 20, 32, 4)])
+def test_workspace_bytes_is_zero_for_rejected_sizes(fn, args):
+    """Sizes the compute calls would reject give 0 (checked before any device query)."""
+    assert getattr(mla.lib(), fn)(*args) == 0
+
+
+@pytest.mark.parametrize("shape", [(4, 4, 16, 1025), (1, 4096, 16, 1088), (64, 1, 128, 512),
+                                   (1, 1, 16, 4)])
+def test_workspace_bytes_matches_workspace_size_for_the_automatic_count(shape):
+    """Both plain-value sizes equal mla_decode_workspace_size with num_partitions = 0;
+    where no device can be queried (a host without a GPU) all three report failure."""
+    out = ctypes.c_size_t(0)
+    st = mla.lib().mla_decode_workspace_size(*shape, 0, ctypes.byref(out))
+    dec = mla.lib().mla_decode_workspace_bytes(*shape)
+    pre = mla.lib().mla_prefill_workspace_bytes(*shape)
+    if st == OK:
+        assert dec == pre == out.value > 0
+    else:
+        assert st == -4 and dec == pre == 0
 
 
 def _counters(B, n_mt):

@@ -231,6 +231,42 @@ def test_uniform_scores():
     assert np.abs(O - O_ref).max() < 1e-5 and np.abs(lse - l_ref).max() < 1e-5
 
 
+def test_rescale_path():
+    """The re-walk case on an E4M3 pool (which takes every block's maximum from its
+    first walk on, so a jump past 32 log2 units over the first block's reference
+    sends the piece straight to the walk from the true maxima).  The pool scale is
+    1/8 so that the x8 keys of the later pages stay exact E4M3 values (no
+    saturation): their codes are re-made with the oracle's quantizer."""
+    from oracle import e4m3_quantize, gather_latent_rows
+    w = e4m3(seed=119, B=2, Sq=4, H=16, lens=("fixed", 64 * 12 + 5), q_sigma=4.0,
+             kv_scale=0.125)
+    codes = w.kv_pool.copy()
+    for b in range(w.B):
+        for p in range(6, 13):
+            page = w.block_table[b, p]
+            vals = e4m3_bits_to_f64(codes[page]) * 8.0  # in code units: exact, below 448
+            nan = np.isnan(vals)
+            new = e4m3_quantize(np.where(nan, 0.0, vals))
+            new[nan] = E4M3_NAN
+            assert np.array_equal(e4m3_bits_to_f64(new)[~nan], vals[~nan])
+            codes[page] = new
+    w.kv_pool = codes
+    pool = E4M3Pool(w.kv_pool, w.kv_scale)
+    q = np.concatenate([w.q_nope.view(np.uint16), w.q_rope.view(np.uint16)], axis=-1)
+    jump = -np.inf
+    for b in range(w.B):
+        rows = gather_latent_rows(pool, w.block_table, b, int(w.seq_lens[b]) - w.Sq + 1)
+        qb = (q[b].reshape(-1, q.shape[-1]).astype(np.uint32) << 16).view(np.float32)
+        s = float(w.scale) * (qb.astype(np.float64) @ rows.T)
+        jump = max(jump, float((s[:, 32:].max(1) - s[:, :32].max(1)).max()) / math.log(2.0))
+    say(f"e4m3 rescale: largest score jump over the first block {jump:.1f} (log2 units)")
+    assert jump > 64.0
+    O_ref, l_ref = oracle(w)
+    for parts in (1, 3):
+        O, lse = run(w, parts=parts)
+        check(O, lse, O_ref, l_ref, f"e4m3 rescale parts={parts}")
+
+
 def test_error_flags_for_bad_pages():
     w = e4m3(seed=232, B=2, Sq=2, H=16, lens=("fixed", 300))
     dev = to_dev(w)

@@ -234,6 +234,43 @@ def test_single_pass_counters_return_to_zero_and_workspace_is_reusable():
     assert mla.read_error_flags(ws) == 0
 
 
+def test_single_pass_counters_after_partials_of_another_shape():
+    """One workspace: a two-pass call at B=2 writes partial results from byte 512, where
+    a B=64 single-pass call keeps its merged-row counters (bytes 512..767); each
+    single-pass call zeroes its counters before it starts, so both following calls
+    merge correctly and leave the counters at zero."""
+    w_small = make_workload("tiny", seed=143, B=2, Sq=4, H=16, lens=("uniform", 1500, 2600))
+    w_big = make_workload("tiny", seed=144, B=64, Sq=1, H=16, lens=("uniform", 100, 900))
+    g_small, g_big = 24, 128
+    need = max(mla.workspace_size(w_small.B, w_small.Sq, w_small.H, w_small.max_pages, g_small),
+               mla.workspace_size(w_big.B, w_big.Sq, w_big.H, w_big.max_pages, g_big))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ds, db = to_dev(w_small), to_dev(w_big)
+    O, lse = mla.decode(ds["q_nope"], ds["q_rope"], ds["kv_pool"], ds["block_table"],
+                        ds["seq_lens"], float(w_small.scale), True, g_small, workspace=ws)
+    torch.cuda.synchronize()
+    check(O.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+          *oracle(w_small), "two-pass B=2")
+    assert _counter_words(ws, w_big.B, 1)[64:].any(), "the B=2 partials did not reach the counters"
+    ref = oracle(w_big)
+    for rnd in range(2):
+        O, lse = mla.decode_single_pass(db["q_nope"], db["q_rope"], db["kv_pool"],
+                                        db["block_table"], db["seq_lens"], float(w_big.scale),
+                                        True, g_big, workspace=ws)
+        torch.cuda.synchronize()
+        assert not _counter_words(ws, w_big.B, 1).any(), f"counters left set (call {rnd})"
+        check(O.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), *ref,
+              f"single-pass B=64 call {rnd}")
+    assert mla.read_error_flags(ws) == 0
+
+
+def test_workspace_bytes_equals_the_automatic_size():
+    for shape in [(4, 4, 16, 1025), (8, 8, 16, 2049), (1, 4096, 16, 1088), (64, 1, 128, 512)]:
+        auto = mla.workspace_size(*shape, 0)
+        assert mla.workspace_bytes(*shape) == auto
+        assert mla.workspace_bytes(*shape, prefill=True) == auto
+
+
 @pytest.mark.parametrize("single", [False, True], ids=["two-pass", "single-pass"])
 @pytest.mark.parametrize("parts", [0, 300, 2100], ids=["G=auto", "G=300", "G=2100"])
 def test_maximum_batch(parts, single):
@@ -315,9 +352,29 @@ def test_uniform_scores():
     assert np.abs(O - O_ref).max() < 1e-5 and np.abs(lse - l_ref).max() < 1e-5
 
 
+def score_jump_log2(w, pool):
+    """Largest amount, in log2 units, by which a folded row's scaled scores over the
+    rows every draft sees rise above the maximum of that row's first 32-row block
+    (the block a piece starting at row 0 takes its exp2 reference from)."""
+    from oracle import gather_latent_rows
+    q = np.concatenate([w.q_nope.view(np.uint16), w.q_rope.view(np.uint16)], axis=-1)
+    jump = -np.inf
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        rows = gather_latent_rows(pool, w.block_table, b, L - w.Sq + 1)
+        qb = (q[b].reshape(-1, q.shape[-1]).astype(np.uint32) << 16).view(np.float32)
+        s = float(w.scale) * (qb.astype(np.float64) @ rows.T)
+        jump = max(jump, float((s[:, 32:].max(1) - s[:, :32].max(1)).max()) / math.log(2.0))
+    return jump
+
+
 def test_rescale_path():
-    """Later pages score far above the first ones (keys x8 and q x4, a jump of tens of
-    nats), which takes the kernel's out-of-loop O rescale path."""
+    """Later pages score far above the first ones (keys x8 and q x4).  A row's exp2
+    reference is the maximum of its first visible block; once a later score passes it
+    by more than 32 (log2 units) the piece is walked again taking every block's
+    maximum, and, since that second walk still starts from the first block's
+    reference, a third time from the true maxima.  The jump here is well past 32, so
+    the whole piece takes all three walks, with one partition and with three."""
     w = make_workload("tiny", seed=119, B=2, Sq=4, H=16, lens=("fixed", 64 * 12 + 5),
                       q_sigma=4.0)
     f = (w.kv_pool.astype(np.uint32) << 16).view(np.float32)
@@ -325,6 +382,9 @@ def test_rescale_path():
         for p in range(6, 13):
             f[w.block_table[b, p]] *= 8.0
     w.kv_pool = f32_to_bf16_bits(f)
+    jump = score_jump_log2(w, w.kv_pool)
+    say(f"rescale: largest score jump over the first block {jump:.1f} (log2 units)")
+    assert jump > 64.0
     O_ref, l_ref = oracle(w)
     for parts in (1, 3):
         O, lse = run(w, parts=parts)
@@ -351,17 +411,54 @@ def test_error_flags_for_bad_lengths_and_pages():
     assert mla.read_error_flags(ws) == 0
 
 
+def test_checked_mode_reports_device_faults(monkeypatch):
+    """MLA_CHECK=1: a call whose seq_lens or block table the kernels had to clamp returns
+    MLA_ERR_DEVICE_CHECK (and clears the flag); a clean call returns MLA_OK."""
+    w = make_workload("tiny", seed=121, B=2, Sq=2, H=16, lens=("fixed", 300))
+    dev = to_dev(w)
+    ws = mla.new_workspace(w.B, w.Sq, w.H, w.max_pages, 2)
+    args = (dev["q_nope"], dev["q_rope"], dev["kv_pool"])
+    monkeypatch.setenv("MLA_CHECK", "1")
+    O, lse = mla.decode(*args, dev["block_table"], dev["seq_lens"], float(w.scale), True, 2,
+                        workspace=ws)
+    check(O.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), *oracle(w),
+          "checked mode, clean call")
+    bad_bt = dev["block_table"].clone()
+    bad_bt[1, 2] = -7
+    with pytest.raises(mla.MLAError) as e:
+        mla.decode(*args, bad_bt, dev["seq_lens"], float(w.scale), True, 2, workspace=ws)
+    assert e.value.status == -5
+    bad_len = dev["seq_lens"].clone()
+    bad_len[0] = 1
+    for fn in (mla.decode, mla.decode_splitkv):
+        with pytest.raises(mla.MLAError) as e:
+            fn(*args, dev["block_table"], bad_len, float(w.scale), True, 2, workspace=ws)
+        assert e.value.status == -5
+    monkeypatch.delenv("MLA_CHECK")
+    assert mla.read_error_flags(ws) == 0  # the checked calls took their flags
+
+
 # ------------------------------------------------------------------------------------
 # Full-size workloads, in the launch configuration the benchmark times (automatic
 # partition count): sampled rows against the oracle computed row by row.
 FULL = ["spec4", "spec8", "spec16", "sweep", "prefill"]
 
 
-def sample_rows(w, rng, n=24):
+def sample_rows(w, rng):
+    """Folded rows checked per request: the first and last row of every 64-row M-tile
+    (so every workgroup of the launch is checked at both ends of its tile), one row
+    of every draft (a random head), and a few random rows.  Every request is
+    sampled.  Prefill (4,096 drafts, 1,024 M-tiles) takes the M-tile ends alone:
+    2,048 rows."""
     M = w.Sq * w.H
     picks = []
-    for b in sorted(set([0, w.B - 1] + rng.integers(0, w.B, size=2).tolist())):
-        ms = set([0, M - 1, M // 2] + rng.integers(0, M, size=n // 4).tolist())
+    for b in range(w.B):
+        ms = set()
+        for mt in range((M + 63) // 64):
+            ms.update([64 * mt, min(M, 64 * mt + 64) - 1])
+        if w.Sq <= 64:
+            ms.update(t * w.H + int(rng.integers(0, w.H)) for t in range(w.Sq))
+            ms.update(rng.integers(0, M, size=4).tolist())
         picks.append((b, sorted(ms)))
     return picks
 
@@ -372,10 +469,16 @@ def test_full_size_sampled(name):
     say(f"{name}: generated, {w.kv_bytes() / 1e9:.2f} GB of latent rows")
     fn = mla.prefill_with_prefix if name == "prefill" else mla.decode
     O, lse = run(w, fn=fn)
+    assert np.isfinite(O).all() and np.isfinite(lse).all()
     rng = np.random.default_rng(7)
     M = w.Sq * w.H
+    n_rows = 0
     for b, ms in sample_rows(w, rng):
-        o_ref, l_ref = mla_attention_rows(w.q_nope, w.q_rope, w.kv_pool, w.block_table,
-                                          w.seq_lens, w.scale, w.causal, b, ms)
-        check(O[b].reshape(M, 512)[ms], lse[b].reshape(M)[ms], o_ref, l_ref, f"{name} b={b}")
-    assert np.isfinite(O).all() and np.isfinite(lse).all()
+        for c0 in range(0, len(ms), 512):  # bounded oracle memory: 512 rows at a time
+            part = ms[c0:c0 + 512]
+            o_ref, l_ref = mla_attention_rows(w.q_nope, w.q_rope, w.kv_pool, w.block_table,
+                                              w.seq_lens, w.scale, w.causal, b, part)
+            check(O[b].reshape(M, 512)[part], lse[b].reshape(M)[part], o_ref, l_ref,
+                  f"{name} b={b} rows {part[0]}..{part[-1]} ({len(part)})")
+            n_rows += len(part)
+    say(f"{name}: {n_rows} rows checked against the oracle")
