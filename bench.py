@@ -10,16 +10,20 @@ like the pages' coding-agent workloads.
 
 Prints one JSON line.  `value` is KV-read throughput: the latent bytes a step must
 read (every visible row once, 576 bf16) divided by the measured time per step.
-`roofline` rates the dominant kernel (the split-KV pass) against its MI355X peak.
-Its duration is the average of per-launch HIP event pairs recorded around each
+`step_us_percentiles` are per-step HIP event pairs over at least 100 steps.
+`roofline` rates the dominant kernel (the split-KV pass) against its MI355X peak:
+its duration is the average of per-launch HIP event pairs recorded around each
 split launch on the stream the kernels run on, in a second run of the same steps
 (the timed steps themselves carry no event markers); like rocprofv3's kernel
-durations, they include each launch's dispatch and end-of-kernel release.  A run of
-back-to-back split launches, where those overlap the neighbouring launches, is
-reported too.  Its `traffic` is the HBM bytes per
-launch measured by rocprofv3 counters (stored under profiles/ and used only while
-the kernel sources are unchanged).  `cpu_baseline`
-times the fp64 CPU oracle on a bounded sample of the same workload.
+durations, they include each launch's dispatch and end-of-kernel release.  Its
+`traffic` is the HBM bytes per launch measured by rocprofv3 counters (stored under
+profiles/ and used only while the kernel sources are unchanged).  `measured_peaks`
+are same-run HIP microbenchmarks (libmla_peaks.so): a 4 GiB streaming read, the
+split kernel's own global->LDS load path, and a bf16 MFMA loop; they run before the
+warm-up, which also brings the clocks up.  With the default workload, the other
+decode configurations of the metric (B=8 and B=16 spec-decode, the H=128 sweep)
+and the prefix prefill are timed too, each as a sub-record with its own roofline.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the main workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -35,6 +39,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "MLA decode µs/step + KV-read HBM GB/s (% peak), B=4/8/16, Sq=4–16, 64K ctx"
+SUB_RECORDS = ["spec8", "spec16", "sweep", "prefill"]
+PERCENTILE_STEPS = 100
 
 
 def log(*a):
@@ -53,7 +59,7 @@ def algorithmic_work(w):
     M = w.Sq * w.H
     pages = int(((L + 63) // 64).sum())
     kv = w.kv_bytes()
-    q = w.B * M * (512 + w.q_rope.shape[3]) * 2
+    q = w.B * M * (512 + w.rope_width) * 2
     out = w.B * M * (512 * 4 + 4)
     bt = pages * 4
     t = np.arange(w.Sq, dtype=np.int64)
@@ -61,7 +67,7 @@ def algorithmic_work(w):
         n_vis = (L[:, None] - w.Sq + t[None, :] + 1).sum()
     else:
         n_vis = L.sum() * w.Sq
-    flops = int(n_vis) * w.H * 2 * (w.kv_pool.shape[2] + 512)
+    flops = int(n_vis) * w.H * 2 * (512 + w.rope_width + 512)
     return dict(kv_bytes=kv, bytes=kv + q + out + bt, flops=flops, pages=pages)
 
 
@@ -119,35 +125,6 @@ def cpu_baseline(w, budget_s=12.0):
             "seconds_per_step_extrapolated": dt * w.B / done}
 
 
-def measured_peaks(torch, dev):
-    """Achievable peaks on this device, for context beside the spec-sheet ones: a plain
-    2 GiB device-to-device copy (bytes read + written per second) and a 8192^3 bf16
-    matmul through torch (hipBLASLt), each timed with events over back-to-back runs."""
-    def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e-3
-    n = 2 << 30
-    src = torch.empty(n, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    t_copy = timed(lambda: dst.copy_(src), 10)
-    del src, dst
-    k = 8192
-    x = torch.randn(k, k, device=dev, dtype=torch.bfloat16)
-    y = torch.randn(k, k, device=dev, dtype=torch.bfloat16)
-    t_mm = timed(lambda: torch.matmul(x, y), 10)
-    del x, y
-    torch.cuda.empty_cache()
-    return {"hbm_copy_GBps": round(2 * n / t_copy / 1e9, 1),
-            "mfma_bf16_matmul_TFLOPs": round(2 * k ** 3 / t_mm / 1e12, 1)}
-
-
 def stored_traffic(config, kv):
     """HBM bytes per split-KV launch from profiles/traffic_<config>[_e4m3|_nope].json,
     if the counters were taken on the current kernel sources (kv: bf16, e4m3 or nope,
@@ -167,12 +144,173 @@ def stored_traffic(config, kv):
     return int(fb + wb)
 
 
+class HostWorkload:
+    """A numpy workload (mla_latent_kv_16_amd.workloads) moved to the device."""
+
+    def __init__(self, w, torch, dev, copies, nope):
+        import numpy as np
+        self.w, self.name = w, w.spec.name
+        self.B, self.Sq, self.H, self.causal = w.B, w.Sq, w.H, w.causal
+        self.seq_lens, self.max_pages, self.scale = w.seq_lens, w.max_pages, float(w.scale)
+        self.rope_width = w.q_rope.shape[3]
+        self.kv_scale = w.kv_scale if w.kv_format == "e4m3" else None
+        self.nope = nope
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        self.q_nope, self.q_rope = t(w.q_nope), t(w.q_rope)
+        if w.kv_format == "e4m3":
+            self.pools = [torch.from_numpy(w.kv_pool).to(dev) for _ in range(copies)]
+        else:
+            self.pools = [t(w.kv_pool) for _ in range(copies)]
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sl = torch.from_numpy(w.seq_lens).to(dev)
+
+    def kv_bytes(self):
+        return self.w.kv_bytes()
+
+
+class DeviceWorkload:
+    """A workload whose lengths and block table follow the numpy recipe (steps 1 and 2,
+    same seed) and whose latent rows and queries are drawn on the device: N(0,1)
+    from torch's seeded device generator, rounded to bf16 (nearest even).  Used for
+    the sub-records, whose multi-GB pools would take tens of seconds to draw on the
+    host.  Every pool page holds finite values (no NaN poison; nothing here checks
+    results)."""
+
+    def __init__(self, name, torch, dev):
+        from mla_latent_kv_16_amd.workloads import DEFAULT_SCALE, draw_layout
+        spec, L, bt, pool_pages = draw_layout(name)
+        self.name, self.B, self.Sq, self.H, self.causal = name, spec.B, spec.Sq, spec.H, spec.causal
+        self.seq_lens, self.max_pages = L.astype("int32"), bt.shape[1]
+        self.scale, self.rope_width, self.kv_scale, self.nope = float(DEFAULT_SCALE), 64, None, False
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + spec.seed)
+        pool = torch.empty((pool_pages, 64, 576), dtype=torch.bfloat16, device=dev)
+        chunk = 2048  # pages per draw: 302 MB of fp32
+        for p0 in range(0, pool_pages, chunk):
+            n = min(chunk, pool_pages - p0)
+            pool[p0:p0 + n] = torch.randn((n, 64, 576), generator=g, device=dev).to(torch.bfloat16)
+        self.pools = [pool.view(torch.int16)]
+        rnd = lambda *shape: torch.randn(shape, generator=g, device=dev).to(
+            torch.bfloat16).view(torch.int16)
+        self.q_nope = rnd(spec.B, spec.Sq, spec.H, 512)
+        self.q_rope = rnd(spec.B, spec.Sq, spec.H, 64)
+        self.bt = torch.from_numpy(bt).to(dev)
+        self.sl = torch.from_numpy(self.seq_lens).to(dev)
+
+    def kv_bytes(self):
+        return int(self.seq_lens.astype("int64").sum()) * 1152
+
+
+def roofline(work, kernel_s, traffic):
+    """The dominant kernel against the roof the step's arithmetic intensity meets first."""
+    hbm = work["bytes"] / kernel_s / 1e9
+    tf = work["flops"] / kernel_s / 1e12
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if work["flops"] / work["bytes"] > ridge:
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic}, hbm, tf
+    return {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(hbm / HBM_PEAK_GBPS, 4), "traffic": traffic}, hbm, tf
+
+
+def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks):
+    """Times one workload: steps (two launches each: split-KV + combine), per-step event
+    percentiles, per-launch split events, and back-to-back split launches."""
+    dev = dw.q_nope.device
+    ws = mla.new_workspace(dw.B, dw.Sq, dw.H, dw.max_pages, G, device=dev)
+    O = torch.empty((dw.B, dw.Sq, dw.H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((dw.B, dw.Sq, dw.H), dtype=torch.float32, device=dev)
+    calls = [mla.BoundDecode(dw.q_nope, dw.q_rope, pool, dw.bt, dw.sl, dw.scale, dw.causal, G, O,
+                             lse, ws, kv_scale=dw.kv_scale, nope=dw.nope) for pool in dw.pools]
+    n = len(calls)
+
+    def step(i):
+        c = calls[i % n]
+        c.splitkv()
+        c.combine()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # the timed steps: nothing but the decode calls between the two synchronisations
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    us_step = (time.perf_counter() - t0) * 1e6 / steps
+    if mla.read_error_flags(ws):
+        raise SystemExit(f"{dw.name}: kernel reported a data fault flag")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # per-step events (split + combine) over at least PERCENTILE_STEPS steps
+    np_steps = max(PERCENTILE_STEPS, steps)
+    sev = [(ev(), ev()) for _ in range(np_steps)]
+    torch.cuda.synchronize()
+    for i in range(np_steps):
+        sev[i][0].record()
+        step(i)
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    step_us = np.array([a.elapsed_time(b) for a, b in sev]) * 1e3
+    # per-launch events around each split launch (the dominant kernel), on its stream
+    kev = [(ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        c = calls[i % n]
+        kev[i][0].record()
+        c.splitkv()
+        kev[i][1].record()
+        c.combine()
+    torch.cuda.synchronize()
+    split_us = np.array([a.elapsed_time(b) for a, b in kev]) * 1e3
+    # the split pass alone, back to back
+    b2b = (ev(), ev())
+    torch.cuda.synchronize()
+    b2b[0].record()
+    for i in range(steps):
+        calls[i % n].splitkv()
+    b2b[1].record()
+    torch.cuda.synchronize()
+    split_b2b = b2b[0].elapsed_time(b2b[1]) * 1e3 / steps
+
+    work = algorithmic_work(dw)
+    split_avg = float(split_us.mean())
+    roof, hbm, tf = roofline(work, split_avg * 1e-6, traffic)
+    if peaks:
+        key = "mfma_bf16_TFLOPs" if roof["bound"] == "mfma" else "lds_dma_stream_GBps"
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / peaks[key], 4)
+        roof["measured_peak_used"] = key
+    rec = {
+        "us_per_step": round(us_step, 2),
+        "kv_GBps_per_step": round(work["kv_bytes"] / (us_step * 1e-6) / 1e9, 1),
+        "kv_frac_of_hbm_peak": round(work["kv_bytes"] / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_us_percentiles": {"steps": int(np_steps),
+                                "median": round(float(np.median(step_us)), 2),
+                                "p10": round(float(np.percentile(step_us, 10)), 2),
+                                "p90": round(float(np.percentile(step_us, 90)), 2)},
+        "split_pass_us": round(split_avg, 2),
+        "split_pass_us_median": round(float(np.median(split_us)), 2),
+        "split_pass_us_p10_p90": [round(float(np.percentile(split_us, 10)), 2),
+                                  round(float(np.percentile(split_us, 90)), 2)],
+        "split_kernel_us_back_to_back": round(split_b2b, 2),
+        "split_pass_hbm_frac": round(hbm / HBM_PEAK_GBPS, 4),
+        "split_pass_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roof,
+    }
+    log(f"{dw.name}: step {us_step:.1f} us (median {rec['step_us_percentiles']['median']:.1f}, "
+        f"p10 {rec['step_us_percentiles']['p10']:.1f}, p90 {rec['step_us_percentiles']['p90']:.1f}"
+        f" over {np_steps}); split pass {split_avg:.1f} us per launch, {split_b2b:.1f} us back to "
+        f"back; split kernel {hbm:.0f} GB/s, {tf:.1f} TFLOP/s ({roof['bound']} frac "
+        f"{roof['frac']})")
+    return rec, calls, ws, work
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400,
-                    help="untimed steps first: the clocks take about 25 ms of load to settle")
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="spec4",
                     help="tiny | spec4 | spec8 | spec16 | sweep | prefill")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "e4m3"],
@@ -184,12 +322,14 @@ def main():
                     help="input copies cycled per step (0 = enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-measured-peaks", action="store_true",
-                    help="skip the copy / matmul measurement of achievable peaks")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the graph-replayed steps")
+                    help="skip the same-run peak microbenchmarks")
+    ap.add_argument("--no-sub-records", action="store_true",
+                    help="time only --config (no spec8 / spec16 / sweep / prefill sub-records)")
     ap.add_argument("--no-single-pass", action="store_true",
                     help="skip the one-launch comparison (profiler runs: every split-KV kernel "
                          "launch is then a split pass alone)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cache-write and absorb/project timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, launch a plain 256 MiB device copy 3 times (counter "
                          "calibration for rocprofv3 --pmc runs)")
@@ -208,116 +348,35 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    torch.cuda.init()
+
+    # same-run peaks first: about a second of sustained load, which also settles the
+    # clocks before the warm-up steps
+    peaks = None
+    if not args.no_measured_peaks:
+        from mla_latent_kv_16_amd import peaks as peaks_mod
+        peaks = peaks_mod.measure(torch, dev)
+        log(f"measured peaks: {peaks}")
+
     t_gen = time.perf_counter()
     if args.nope and args.kv != "bf16":
         raise SystemExit("--nope pools are bf16")
     w = make_workload(args.config, kv_format=args.kv, rope=not args.nope)
-    work = algorithmic_work(w)
-    log(f"{args.config} ({args.kv} pool): B={w.B} Sq={w.Sq} H={w.H} pages={work['pages']} "
-        f"kv={work['kv_bytes'] / 1e6:.1f} MB, generated in {time.perf_counter() - t_gen:.1f}s")
-
+    kv_main = w.kv_bytes()
     # Cycle over independent copies of the pool so that consecutive steps cannot be
     # served from the 256 MB MALL left warm by the previous step.
-    pool_bytes = w.kv_pool.nbytes
-    n_copies = args.rotate or max(1, min(4, int(np.ceil(2 * 256e6 / max(work["kv_bytes"], 1))) + 1))
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
-    q_nope, q_rope = t(w.q_nope), t(w.q_rope)
-    if args.kv == "e4m3":
-        pools = [torch.from_numpy(w.kv_pool).to(dev) for _ in range(n_copies)]
-        kv_scale = w.kv_scale
-    else:
-        pools = [t(w.kv_pool) for _ in range(n_copies)]
-        kv_scale = None
-    bt = torch.from_numpy(w.block_table).to(dev)
-    sl = torch.from_numpy(w.seq_lens).to(dev)
+    n_copies = args.rotate or max(1, min(4, int(np.ceil(2 * 256e6 / max(kv_main, 1))) + 1))
+    hw = HostWorkload(w, torch, dev, n_copies, args.nope)
+    log(f"{args.config} ({args.kv} pool): B={w.B} Sq={w.Sq} H={w.H} "
+        f"kv={kv_main / 1e6:.1f} MB, generated in {time.perf_counter() - t_gen:.1f}s, "
+        f"{n_copies} pool copies")
     G = args.partitions or mla.auto_partitions(w.B, w.Sq, w.H, w.max_pages)
-    ws = mla.new_workspace(w.B, w.Sq, w.H, w.max_pages, G, device=dev)
-    O = torch.empty((w.B, w.Sq, w.H, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.B, w.Sq, w.H), dtype=torch.float32, device=dev)
-    scale = float(w.scale)
-    log(f"partitions={G} pool copies={n_copies} ({pool_bytes / 1e9:.2f} GB each)")
+    traffic = stored_traffic(args.config, "nope" if args.nope else args.kv)
+    main_rec, calls, ws, work = time_workload(torch, np, mla, hw, G, args.steps, args.warmup,
+                                              traffic, peaks)
+    O = calls[0].out
 
-    calls = [mla.BoundDecode(q_nope, q_rope, pool, bt, sl, scale, w.causal, G, O, lse, ws,
-                             kv_scale=kv_scale, nope=args.nope) for pool in pools]
-
-    def step(i, ev=None):
-        c = calls[i % n_copies]
-        if ev is not None:
-            ev[0].record()
-        c.splitkv()
-        if ev is not None:
-            ev[1].record()
-        c.combine()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # The timed steps: nothing but the decode calls between the two synchronisations.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    if mla.read_error_flags(ws):
-        raise SystemExit("kernel reported a data fault flag")
-
-    # Per-launch split durations, from a second run of the same steps with events
-    # around each split launch.  The library launches on torch's current stream, where
-    # these events are recorded.  An event adds a marker to the stream, so this run is
-    # kept out of the timed steps.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    split_ms = [a.elapsed_time(b) for a, b in evs]
-    split_avg = float(np.mean(split_ms))
-
-    # The dominant kernel alone: the split pass launched back to back over the same
-    # rotation of pools, two events around the whole run.  Per-launch events around
-    # each split inside the steps also count the dispatch of the launch and the
-    # release at its end; back to back, those overlap the neighbouring launches.
-    kev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    torch.cuda.synchronize()
-    kev[0].record()
-    for i in range(args.steps):
-        calls[i % n_copies].splitkv()
-    kev[1].record()
-    torch.cuda.synchronize()
-    split_b2b = kev[0].elapsed_time(kev[1]) / args.steps
-
-    # The same steps replayed from HIP graphs (one captured step per pool copy), as a
-    # serving loop that captures its decode step would run them.
-    graph_us = None
-    if not args.no_graph:
-        gs = torch.cuda.Stream()
-        gcalls = [mla.BoundDecode(q_nope, q_rope, pool, bt, sl, scale, w.causal, G, O, lse, ws,
-                                  stream=gs, kv_scale=kv_scale, nope=args.nope) for pool in pools]
-        graphs = []
-        with torch.cuda.stream(gs):
-            for c in gcalls:
-                c()
-        torch.cuda.synchronize()
-        for c in gcalls:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=gs):
-                c()
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % n_copies].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % n_copies].replay()
-        torch.cuda.synchronize()
-        graph_us = (time.perf_counter() - t0) * 1e6 / args.steps
-        del graphs, gcalls
-
-    # The same steps in one launch each (mla_decode_single_pass), for comparison.
+    # the same steps in one launch each (mla_decode_single_pass), for comparison
     single_pass_us = None
     if G > 1 and not args.no_single_pass and not args.nope:
         torch.cuda.synchronize()
@@ -338,15 +397,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # The cache write of a step's new rows (mla_kv_append[_e4m3]), timed back to back
-    # after every decode timing (it rewrites the draft rows of the pools); the write
-    # takes 576-wide rows, so NoPE pools skip it.
     append_us = append_bytes = None
-    if not args.nope:
+    gemm = {}
+    if not args.nope and not args.no_extras:
+        # the cache write of a step's new rows (mla_kv_append[_e4m3]), back to back after
+        # every decode timing (it rewrites the draft rows of the pools)
         kv_new = torch.from_numpy(f32_to_bf16_bits(np.random.default_rng(1).standard_normal(
             (w.B, w.Sq, 576)).astype(np.float32)).view(np.int16)).to(dev)
         app_ws = torch.zeros(256, dtype=torch.uint8, device=dev)
-        appends = [mla.bound_kv_append(kv_new, p, bt, sl, app_ws, kv_scale) for p in pools]
+        appends = [mla.bound_kv_append(kv_new, p, hw.bt, hw.sl, app_ws, hw.kv_scale)
+                   for p in hw.pools]
         for i in range(3):
             appends[i % n_copies]()
         aev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -360,11 +420,8 @@ def main():
         if mla.read_error_flags(app_ws):
             raise SystemExit("kv append reported a data fault flag")
         append_bytes = w.B * w.Sq * 576 * (2 + w.row_bytes // 576)
-
-    # The GEMMs around the attention for this batch's shape (absorb before, project
-    # after), with seeded random weights, timed back to back.
-    gemm = {}
-    if not args.nope:
+        # the GEMMs around the attention for this batch's shape (absorb before, project
+        # after), with seeded random weights, timed back to back
         g_rng = np.random.default_rng(2)
         bfw = lambda shape, sc: torch.from_numpy(f32_to_bf16_bits(
             (g_rng.standard_normal(shape) * sc).astype(np.float32)).view(np.int16)).to(dev)
@@ -386,41 +443,38 @@ def main():
             us = gev[0].elapsed_time(gev[1]) / 20 * 1e3
             gemm[f"{tag}_us"] = round(us, 2)
             gemm[f"{tag}_TFLOPs"] = round(2 * rows_h * 128 * 512 / (us * 1e-6) / 1e12, 2)
+    del calls, hw
+    torch.cuda.empty_cache()
 
-    peaks = None if args.no_measured_peaks else measured_peaks(torch, dev)
-
-    value = work["kv_bytes"] / (ms_step * 1e-3) / 1e9
-    # the dominant kernel's average launch duration: per-launch events on its stream
-    hbm_achieved = work["bytes"] / (split_avg * 1e-3) / 1e9
-    mfma_achieved = work["flops"] / (split_avg * 1e-3) / 1e12
-    traffic = stored_traffic(args.config, "nope" if args.nope else args.kv)
-    # the bound is the roof the step's arithmetic intensity meets first
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    mfma_bound = work["flops"] / work["bytes"] > ridge
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(mfma_achieved, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "hbm", "achieved": round(hbm_achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic}
-    if peaks:
-        key = "mfma_bf16_matmul_TFLOPs" if mfma_bound else "hbm_copy_GBps"
-        roof["frac_of_measured_peak"] = round(roof["achieved"] / peaks[key], 4)
-    log(f"step {ms_step * 1e3:.1f} us (split pass {split_avg * 1e3:.1f} us with per-launch events, "
-        f"median {np.median(split_ms) * 1e3:.1f} p10 {np.percentile(split_ms, 10) * 1e3:.1f} "
-        f"p90 {np.percentile(split_ms, 90) * 1e3:.1f}; "
-        f"{split_b2b * 1e3:.1f} us back to back); {value:.0f} GB/s of KV; split kernel "
-        f"{hbm_achieved:.0f} GB/s, {mfma_achieved:.1f} TFLOP/s")
+    # the metric's other configurations, timed in the same run
+    subs = {}
+    if (args.config == "spec4" and args.kv == "bf16" and not args.nope
+            and not args.no_sub_records):
+        for name in SUB_RECORDS:
+            t_gen = time.perf_counter()
+            dw = DeviceWorkload(name, torch, dev)
+            Gs = mla.auto_partitions(dw.B, dw.Sq, dw.H, dw.max_pages)
+            log(f"{name}: B={dw.B} Sq={dw.Sq} H={dw.H} kv={dw.kv_bytes() / 1e6:.1f} MB, drawn "
+                f"on the device in {time.perf_counter() - t_gen:.1f}s, partitions={Gs}")
+            sub_steps = max(20, min(args.steps, 100))
+            rec, c2, _, wk = time_workload(torch, np, mla, dw, Gs, sub_steps, 10,
+                                           stored_traffic(name, "bf16"), peaks)
+            rec = {"config": {"workload": name, "B": dw.B, "Sq": dw.Sq, "H": dw.H,
+                              "context": [int(dw.seq_lens.min()), int(dw.seq_lens.max())],
+                              "partitions": Gs, "kv_bytes": wk["kv_bytes"],
+                              "tflops_per_step": wk["flops"] / 1e12},
+                   "steps": sub_steps, **rec}
+            subs[name] = rec
+            del c2, dw
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        del pools, calls
-        torch.cuda.empty_cache()
         cpu = cpu_baseline(w)
         log(f"cpu oracle: {cpu['value']:.4f} GB/s on {cpu['cores']} threads ({cpu['sample']})")
 
+    us_step = main_rec["us_per_step"]
+    value = work["kv_bytes"] / (us_step * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -428,8 +482,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "us_per_step": round(ms_step * 1e3, 2),
+        "ms_per_step": round(us_step * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -445,22 +498,14 @@ def main():
                                            else "bf16")),
                    "partitions": G,
                    "kv_bytes": work["kv_bytes"], "tflops_per_step": work["flops"] / 1e12},
-        "kv_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-        "split_pass_us": round(split_avg * 1e3, 2),
-        "split_pass_us_median": round(float(np.median(split_ms)) * 1e3, 2),
-        "split_pass_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
-                                  round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
-        "split_kernel_us_back_to_back": round(split_b2b * 1e3, 2),
-        "us_per_step_graph_replay": None if graph_us is None else round(graph_us, 2),
+        **main_rec,
         "single_pass_us_per_step": None if single_pass_us is None else round(single_pass_us, 2),
-        "split_pass_hbm_frac": round(hbm_achieved / HBM_PEAK_GBPS, 4),
-        "split_pass_mfma_frac": round(mfma_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "kv_append_us": None if append_us is None else round(append_us, 2),
         "kv_append_GBps": (None if append_us is None
                            else round(append_bytes / (append_us * 1e-6) / 1e9, 2)),
         "absorb_project": gemm or None,
-        "roofline": roof,
         "measured_peaks": peaks,
+        "sub_records": subs or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

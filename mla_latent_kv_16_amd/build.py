@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = ["mla_api.hip", "mla_kernels.hip", "mla_append.hip", "mla_project.hip"]
+# the achievable-peak microbenchmarks the benchmark measures its denominators with
+PEAKS_LIB = os.path.join(PKG, "libmla_peaks.so")
+PEAKS_SOURCES = ["mla_peaks.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -36,10 +39,16 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = True, extra=()) -> str:
-    """Compiles every HIP source into libmla.so next to this file; returns its path."""
-    tmp = LIB + ".tmp"
+    """Compiles libmla.so (the attention path) and libmla_peaks.so (the peak
+    microbenchmarks) next to this file; returns the path of libmla.so."""
+    _build_one(PEAKS_LIB, PEAKS_SOURCES, verbose, extra)
+    return _build_one(LIB, SOURCES, verbose, extra)
+
+
+def _build_one(lib: str, sources, verbose: bool, extra) -> str:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,8 +58,8 @@ def build(verbose: bool = True, extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
@@ -60,7 +69,7 @@ if __name__ == "__main__":
         extra = ["-save-temps=obj", "-o"]  # placeholder, handled below
         cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
                "--cuda-device-only", "-S"]
-        for s in SOURCES:
+        for s in SOURCES + PEAKS_SOURCES:
             out = os.path.join(sys.argv[2], s.replace(".hip", ".s"))
             subprocess.run(cmd + [os.path.join(CSRC, s), "-o", out], check=True)
             print(out)

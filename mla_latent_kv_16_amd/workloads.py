@@ -181,6 +181,24 @@ def _draw_lens(spec: WorkloadSpec, rng: np.random.Generator, B: int) -> np.ndarr
     raise ValueError(kind)
 
 
+def draw_layout(spec_or_name):
+    """Steps 1 and 2 of the recipe alone: (spec, L int64 [B], block_table int32
+    [B, max_pages], pool_pages), with the same draws make_workload takes first."""
+    spec = WORKLOADS[spec_or_name] if isinstance(spec_or_name, str) else spec_or_name
+    rng = np.random.default_rng(spec.seed)
+    L = _draw_lens(spec, rng, spec.B)
+    pages_per = (L + PAGE - 1) // PAGE
+    pool_pages = max(1, 2 * int(pages_per.sum()))
+    perm = rng.permutation(pool_pages).astype(np.int32)
+    block_table = np.full((spec.B, max(1, int(pages_per.max()))), -1, dtype=np.int32)
+    off = 0
+    for b in range(spec.B):
+        n = int(pages_per[b])
+        block_table[b, :n] = perm[off:off + n]
+        off += n
+    return spec, L, block_table, pool_pages
+
+
 def make_workload(spec_or_name, *, seed: Optional[int] = None, B: Optional[int] = None,
                   Sq: Optional[int] = None, H: Optional[int] = None,
                   lens=None, causal: Optional[bool] = None,

@@ -39,9 +39,32 @@ def test_library_exports_every_header_function():
     assert set(names) <= exported
 
 
-def test_header_compiles_as_c():
-    hdr = os.path.join(os.path.dirname(mla.LIB_PATH), "..", "include", "mla.h")
-    src = f'#include "{os.path.abspath(hdr)}"\nint main(void) {{ return MLA_OK; }}\n'
+def test_peaks_library_exports_its_header():
+    """libmla_peaks.so (measurement support) exports every function mla_peaks.h declares
+    and rejects bad arguments on the host (nothing is launched)."""
+    from mla_latent_kv_16_amd import peaks
+    hdr = os.path.join(os.path.dirname(mla.LIB_PATH), "..", "include", "mla_peaks.h")
+    names = bnd.header_functions(hdr)
+    assert names == sorted(["mla_peak_stream_read", "mla_peak_dma_stream",
+                            "mla_peak_dma_stream_bytes", "mla_peak_mfma_bf16",
+                            "mla_peak_mfma_bf16_flops"])
+    out = subprocess.run(["nm", "-D", "--defined-only", peaks.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+    L = peaks.lib()
+    assert L.mla_peak_stream_read(None, 1 << 20, FAKE, 8, None) == -1
+    assert L.mla_peak_stream_read(FAKE + 4, 1 << 20, FAKE, 8, None) == -1
+    assert L.mla_peak_dma_stream(FAKE, 1000, FAKE, 8, None) == -1  # under one block each
+    assert L.mla_peak_mfma_bf16(0, FAKE, 8, None) == -1
+    assert L.mla_peak_dma_stream_bytes(36864 * 10 + 5, 3) == 36864 * 9
+    assert L.mla_peak_mfma_bf16_flops(10, 2) == 2 * 4 * 10 * 4 * 32768
+
+
+@pytest.mark.parametrize("header", ["mla.h", "mla_peaks.h"])
+def test_header_compiles_as_c(header):
+    hdr = os.path.join(os.path.dirname(mla.LIB_PATH), "..", "include", header)
+    src = f'#include "{os.path.abspath(hdr)}"\nint main(void) {{ return 0; }}\n'
     res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-x", "c", "-", "-o", "/dev/null"],
                          input=src, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
