@@ -152,6 +152,29 @@ int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* k
                float* O, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Its workspace is a static 64 MiB device array inside the library, one
+ * per GPU, held until the process ends; the library looks up its address once per
+ * device and allocates nothing.  Same arguments, meaning and results as mla_decode
+ * (bit for bit at the same partition count), minus workspace and workspace_bytes:
+ *   num_partitions = 0  the automatic count, lowered where needed so that the
+ *                       partial results fit the array (1 always fits)
+ *   num_partitions > 0  that count; MLA_ERR_WORKSPACE if its partial results
+ *                       (mla_decode_workspace_size) exceed 64 MiB, before anything
+ *                       is enqueued
+ * Every call on one GPU shares that GPU's array and leaves its contents behind
+ * (each call writes every partial it reads), so calls that overlap on one GPU, on
+ * any streams, race: a caller serialises them.  Data-fault flags land in the
+ * array's header, where only checked mode (MLA_CHECK=1) reads them.
+ */
+int mla_decode_noalloc(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                       int64_t num_pages, int page_size, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
+                       float softmax_scale, int causal, int num_partitions, float* O,
+                       float* lse, void* stream);
+
+/*
  * The same decode in ONE launch ("Faster kernels, slower engine", §7.1: a
  * hand-written kernel can skip the second pass).  Workgroups appended to the
  * split-KV grid merge each request's partials as soon as its pieces have published

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     decode_combine,
     decode_e4m3,
     decode_nope,
+    decode_noalloc,
     decode_single_pass,
     decode_single_pass_e4m3,
     decode_splitkv,

@@ -50,6 +50,7 @@ _SIGNATURES = {
     "mla_prefill_with_prefix": (_COMPUTE_ARGS, _i32),
     "mla_decode_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_single_pass": (_COMPUTE_ARGS, _i32),
+    "mla_decode_noalloc": (_COMPUTE_ARGS[:16] + [_vp], _i32),
     "mla_kv_append": ([_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp], _i32),
     "mla_kv_append_e4m3": ([_vp, _vp, _f32, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _sz,
                             _vp], _i32),
@@ -263,6 +264,23 @@ def decode(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal
     """mla_decode: split-KV pass + combine pass.  Returns (O fp32 [B,Sq,H,512], lse fp32 [B,Sq,H])."""
     return _compute("mla_decode", q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale,
                     causal, num_partitions, out, lse, workspace, stream)
+
+
+def decode_noalloc(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale, causal=True,
+                   num_partitions=0, out=None, lse=None, stream=None):
+    """mla_decode_noalloc: the decode with its workspace in the library's own static
+    device array (no workspace argument, nothing allocated by the library)."""
+    torch = _torch()
+    B, Sq, H, _ = q_nope.shape
+    ws = torch.empty(256, dtype=torch.uint8, device=q_nope.device)  # validation only
+    B, Sq, H, maxp, out, lse, _ = _prep(q_nope, q_rope, kv_pool, block_table, seq_lens, out, lse,
+                                        ws, 1)
+    st = lib().mla_decode_noalloc(_ptr(q_nope), _ptr(q_rope), _ptr(kv_pool), kv_pool.shape[0],
+                                  PAGE_SIZE, _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H,
+                                  float(softmax_scale), 1 if causal else 0, int(num_partitions),
+                                  _ptr(out), _ptr(lse), _stream_handle(stream))
+    _check(st, "mla_decode_noalloc")
+    return out, lse
 
 
 def decode_single_pass(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale,

@@ -314,6 +314,41 @@ int decode_call(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_p
   return finish(st, workspace, s);
 }
 
+// ---- the no-allocation decode ------------------------------------------------------
+// mla_decode_noalloc keeps its workspace (error-flag header, partial results) in this
+// file-scope device array instead of a caller buffer.  Each device the library runs on
+// holds its own copy until the process ends.  In host code the array's name is only a
+// host-side stand-in: the device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch, and only that address is ever passed on.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+void* g_scratch[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  if (!g_scratch[dev]) return MLA_ERR_HIP;
+  *out = g_scratch[dev];
+  return MLA_OK;
+}
+
+// Largest partition count <= G whose workspace fits the scratch array (1 always
+// fits: a call without a split needs only the header).
+int partitions_fitting(const Geometry& g, int B, int G) {
+  while (G > 1 && workspace_bytes_for(g, B, G) > kScratchBytes) {
+    const size_t piece = (size_t)g.n_mt * g.slot_rows * (kNope + 1) * sizeof(float);
+    const size_t fixed = kHeaderBytes + counter_bytes(g, B) + 256;
+    const int64_t fit = kScratchBytes > fixed ? (int64_t)((kScratchBytes - fixed) / piece) - B : 0;
+    G = fit >= 2 && fit < G ? (int)fit : (fit < 2 ? 1 : G - 1);
+  }
+  return G;
+}
+
 }  // namespace
 
 extern "C" {
@@ -427,6 +462,29 @@ int mla_decode(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* k
   return decode_call(q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, page_size, block_table,
                      max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal,
                      num_partitions, O, lse, workspace, workspace_bytes, stream, false);
+}
+
+int mla_decode_noalloc(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* kv_pool,
+                       int64_t num_pages, int page_size, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* seq_lens, int B, int Sq, int H,
+                       float softmax_scale, int causal, int num_partitions, float* O,
+                       float* lse, void* stream) {
+  Geometry g;
+  int st = geometry(B, Sq, H, max_pages_per_seq, &g);
+  if (st != MLA_OK) return st;
+  int G = 0;
+  st = resolve_partitions(g, B, max_pages_per_seq, num_partitions, &G);
+  if (st != MLA_OK) return st;
+  if (num_partitions == 0)
+    G = partitions_fitting(g, B, G);
+  else if (workspace_bytes_for(g, B, G) > kScratchBytes)
+    return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MLA_OK) return st;
+  return decode_call(q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages, page_size,
+                     block_table, max_pages_per_seq, seq_lens, B, Sq, H, softmax_scale, causal, G,
+                     O, lse, ws, kScratchBytes, stream, false);
 }
 
 int mla_decode_single_pass(const uint16_t* q_nope, const uint16_t* q_rope,

@@ -23,7 +23,7 @@ def test_library_exports_every_header_function():
     assert names == sorted([
         "mla_absorb_q", "mla_project_o",
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
-        "mla_decode_nope", "mla_decode_splitkv_nope",
+        "mla_decode_nope", "mla_decode_noalloc", "mla_decode_splitkv_nope",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
         "mla_decode_splitkv_e4m3", "mla_decode_splitkv_placement", "mla_decode_tree",
         "mla_decode_tree_e4m3",
