@@ -206,6 +206,17 @@ int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool,
   return MLA_OK;
 }
 
+// Which split-KV kernel runs a call: the eight-wave one where it applies (bf16 pools
+// without draft trees, two-pass calls) and is chosen, else the four-wave one.
+// MLA_SPLITKV=4 or =8 in the environment forces the choice where both apply.
+bool use_splitkv8(const SplitArgs& a) {
+  if (a.kv_e4m3 || a.kv_nope || a.tree_mask || a.arrive || a.wg_trace) return false;
+  const char* v = getenv("MLA_SPLITKV");
+  if (v && v[0] == '8' && v[1] == 0) return true;
+  if (v && v[0] == '4' && v[1] == 0) return false;
+  return false;
+}
+
 int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
                   const void* kv_pool, int kv_format, float kv_scale, int64_t num_pages,
                   const int32_t* block_table, int max_pages, const int32_t* seq_lens,
@@ -263,7 +274,8 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
     if (launch_clear_words(c.lay.arrive, 2 * (int64_t)B * c.geo.n_mt, stream) != hipSuccess)
       return MLA_ERR_HIP;
   }
-  return launch_splitkv(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  const hipError_t e = use_splitkv8(a) ? launch_splitkv8(a, stream) : launch_splitkv(a, stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int enqueue_combine(const Call& c, const int32_t* seq_lens, int max_pages, int B, int Sq, int H,
