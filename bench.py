@@ -144,6 +144,17 @@ def stored_traffic(config, kv):
     return int(fb + wb)
 
 
+def scale_later_pages(w, first, factor):
+    """Multiplies the bf16 latent rows of logical pages >= `first` of every request by
+    `factor` (a power of two, so exactly), in place."""
+    import numpy as np
+    from mla_latent_kv_16_amd.workloads import f32_to_bf16_bits
+    pages = np.unique(w.block_table[:, first:][w.block_table[:, first:] >= 0])
+    for chunk in np.array_split(pages, max(1, len(pages) // 256)):
+        f = (w.kv_pool[chunk].astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+        w.kv_pool[chunk] = f32_to_bf16_bits(f)
+
+
 class HostWorkload:
     """A numpy workload (mla_latent_kv_16_amd.workloads) moved to the device."""
 
@@ -330,6 +341,11 @@ def main():
                          "launch is then a split pass alone)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the cache-write and absorb/project timings")
+    ap.add_argument("--rescale", action="store_true",
+                    help="worst case of the exp2 reference: keys of every page from the seventh "
+                         "on scaled by 8 and queries drawn N(0, 4^2), so that later scores pass "
+                         "the first block's reference by far more than 32 (log2) and each piece is "
+                         "walked three times (bf16 pools)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, launch a plain 256 MiB device copy 3 times (counter "
                          "calibration for rocprofv3 --pmc runs)")
@@ -361,7 +377,12 @@ def main():
     t_gen = time.perf_counter()
     if args.nope and args.kv != "bf16":
         raise SystemExit("--nope pools are bf16")
-    w = make_workload(args.config, kv_format=args.kv, rope=not args.nope)
+    w = make_workload(args.config, kv_format=args.kv, rope=not args.nope,
+                      q_sigma=4.0 if args.rescale else None)
+    if args.rescale:
+        if args.kv != "bf16":
+            raise SystemExit("--rescale takes bf16 pools")
+        scale_later_pages(w, first=6, factor=8.0)
     kv_main = w.kv_bytes()
     # Cycle over independent copies of the pool so that consecutive steps cannot be
     # served from the 256 MB MALL left warm by the previous step.
