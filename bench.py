@@ -10,7 +10,8 @@ like the pages' coding-agent workloads.
 
 Prints one JSON line.  `value` is KV-read throughput: the latent bytes a step must
 read (every visible row once, 576 bf16) divided by the measured time per step.
-`step_us_percentiles` are per-step HIP event pairs over at least 100 steps.
+`step_us_percentiles` come from HIP events recorded between consecutive steps, over
+at least 100 steps and at least a second of them.
 `roofline` rates the dominant kernel (the split-KV pass) against its MI355X peak:
 its duration is the average of per-launch HIP event pairs recorded around each
 split launch on the stream the kernels run on, in a second run of the same steps
@@ -41,6 +42,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "MLA decode µs/step + KV-read HBM GB/s (% peak), B=4/8/16, Sq=4–16, 64K ctx"
 SUB_RECORDS = ["spec8", "spec16", "sweep", "prefill"]
 PERCENTILE_STEPS = 100
+PERCENTILE_SECONDS = 1.0
+PERCENTILE_MAX_STEPS = 20000
 
 
 def log(*a):
@@ -225,7 +228,8 @@ def roofline(work, kernel_s, traffic):
             "frac": round(hbm / HBM_PEAK_GBPS, 4), "traffic": traffic}, hbm, tf
 
 
-def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks):
+def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks,
+                  percentile_seconds=PERCENTILE_SECONDS):
     """Times one workload: steps (two launches each: split-KV + combine), per-step event
     percentiles, per-launch split events, and back-to-back split launches."""
     dev = dw.q_nope.device
@@ -254,16 +258,18 @@ def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks):
         raise SystemExit(f"{dw.name}: kernel reported a data fault flag")
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    # per-step events (split + combine) over at least PERCENTILE_STEPS steps
-    np_steps = max(PERCENTILE_STEPS, steps)
-    sev = [(ev(), ev()) for _ in range(np_steps)]
+    # step durations between consecutive events (one event per step boundary) over at
+    # least PERCENTILE_STEPS steps and at least percentile_seconds of steps
+    np_steps = int(max(PERCENTILE_STEPS, steps,
+                       min(PERCENTILE_MAX_STEPS, percentile_seconds / (us_step * 1e-6))))
+    marks = [ev() for _ in range(np_steps + 1)]
     torch.cuda.synchronize()
+    marks[0].record()
     for i in range(np_steps):
-        sev[i][0].record()
         step(i)
-        sev[i][1].record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    step_us = np.array([a.elapsed_time(b) for a, b in sev]) * 1e3
+    step_us = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(np_steps)]) * 1e3
     # per-launch events around each split launch (the dominant kernel), on its stream
     kev = [(ev(), ev()) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -321,6 +327,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--percentile-seconds", type=float, default=PERCENTILE_SECONDS,
+                    help="least span of steps behind the step percentiles (at least 100 "
+                         "steps are always timed); a profiled run passes 0 to keep its "
+                         "traces short")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="spec4",
                     help="tiny | spec4 | spec8 | spec16 | sweep | prefill")
@@ -366,14 +376,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.init()
 
-    # same-run peaks first: about a second of sustained load, which also settles the
-    # clocks before the warm-up steps
-    peaks = None
-    if not args.no_measured_peaks:
-        from mla_latent_kv_16_amd import peaks as peaks_mod
-        peaks = peaks_mod.measure(torch, dev)
-        log(f"measured peaks: {peaks}")
-
     t_gen = time.perf_counter()
     if args.nope and args.kv != "bf16":
         raise SystemExit("--nope pools are bf16")
@@ -393,8 +395,15 @@ def main():
         f"{n_copies} pool copies")
     G = args.partitions or mla.auto_partitions(w.B, w.Sq, w.H, w.max_pages)
     traffic = stored_traffic(args.config, "nope" if args.nope else args.kv)
+    # same-run peaks right before the timed work: about a second of sustained load,
+    # which also settles the clocks that the host-side input generation let drop
+    peaks = None
+    if not args.no_measured_peaks:
+        from mla_latent_kv_16_amd import peaks as peaks_mod
+        peaks = peaks_mod.measure(torch, dev)
+        log(f"measured peaks: {peaks}")
     main_rec, calls, ws, work = time_workload(torch, np, mla, hw, G, args.steps, args.warmup,
-                                              traffic, peaks)
+                                              traffic, peaks, args.percentile_seconds)
     O = calls[0].out
 
     # the same steps in one launch each (mla_decode_single_pass), for comparison
@@ -477,9 +486,10 @@ def main():
             Gs = mla.auto_partitions(dw.B, dw.Sq, dw.H, dw.max_pages)
             log(f"{name}: B={dw.B} Sq={dw.Sq} H={dw.H} kv={dw.kv_bytes() / 1e6:.1f} MB, drawn "
                 f"on the device in {time.perf_counter() - t_gen:.1f}s, partitions={Gs}")
-            sub_steps = max(20, min(args.steps, 100))
-            rec, c2, _, wk = time_workload(torch, np, mla, dw, Gs, sub_steps, 10,
-                                           stored_traffic(name, "bf16"), peaks)
+            sub_steps = 100
+            rec, c2, _, wk = time_workload(torch, np, mla, dw, Gs, sub_steps, 50,
+                                           stored_traffic(name, "bf16"), peaks,
+                                           args.percentile_seconds)
             rec = {"config": {"workload": name, "B": dw.B, "Sq": dw.Sq, "H": dw.H,
                               "context": [int(dw.seq_lens.min()), int(dw.seq_lens.max())],
                               "partitions": Gs, "kv_bytes": wk["kv_bytes"],
@@ -518,7 +528,9 @@ def main():
                               "512+64 " + ("e4m3, per-tensor scale" if args.kv == "e4m3"
                                            else "bf16")),
                    "partitions": G,
-                   "kv_bytes": work["kv_bytes"], "tflops_per_step": work["flops"] / 1e12},
+                   "kv_bytes": work["kv_bytes"], "tflops_per_step": work["flops"] / 1e12,
+                   **({"values": "worst case of the exp2 reference: keys of pages 7 on x8, "
+                                 "queries N(0, 4^2)"} if args.rescale else {})},
         **main_rec,
         "single_pass_us_per_step": None if single_pass_us is None else round(single_pass_us, 2),
         "kv_append_us": None if append_us is None else round(append_us, 2),

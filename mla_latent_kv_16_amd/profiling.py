@@ -129,23 +129,84 @@ def counters_table(paths) -> str:
     return "\n".join(out)
 
 
+# Normalisation of the SQ/GRBM counters on this chip (8 XCDs, 32 CUs and 128 SIMDs
+# each), checked against the split kernel's own algorithmic flops at prefill, where
+# SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 equals them:
+#   GRBM_GUI_ACTIVE            GPU-busy cycles summed over the 8 XCDs
+#   SQ_VALU_MFMA_BUSY_CYCLES   matrix-core busy cycles summed over all 1,024 SIMDs
+#   SQ_WAVE_CYCLES, SQ_BUSY_CU_CYCLES, SQ_WAIT_*, SQ_ACTIVE_INST_*
+#                              wave-resident cycles summed over waves, in units of 4
+XCDS = 8
+SIMDS = 1024
+
+
+def derived_table(paths) -> str:
+    """Per-kernel figures derived from the averaged counters, with the normalisation
+    above: clock cycles per XCD, matrix-core busy share of SIMD cycles, instructions
+    per MFMA, and shares of wave-resident time."""
+    per = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        for r in _rows(path):
+            per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = ["| kernel | figure | value | from |", "|---|---|---|---|"]
+    for k in sorted(per):
+        if "copy" in k.lower() or "elementwise" in k.lower():
+            continue
+        c = {n: sum(v) / len(v) for n, v in per[k].items()}
+        name = f"`{k[:60]}`"
+        cyc = c.get("GRBM_GUI_ACTIVE")
+        if cyc:
+            out.append(f"| {name} | GPU-busy cycles per XCD | {cyc / XCDS:.4g} | GRBM_GUI_ACTIVE / 8 |")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                out.append(f"| {name} | matrix cores busy, share of SIMD cycles | "
+                           f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc / XCDS * SIMDS):.1%} | "
+                           f"SQ_VALU_MFMA_BUSY_CYCLES / (1024 x GRBM_GUI_ACTIVE / 8) |")
+            if "SQ_WAVE_CYCLES" in c:
+                out.append(f"| {name} | waves resident per SIMD (average) | "
+                           f"{4 * c['SQ_WAVE_CYCLES'] / (cyc / XCDS * SIMDS):.3g} | "
+                           f"4 x SQ_WAVE_CYCLES / (1024 x GRBM_GUI_ACTIVE / 8) |")
+        mf = c.get("SQ_INSTS_MFMA")
+        if mf:
+            for n in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM"):
+                if n in c:
+                    out.append(f"| {name} | {n} per MFMA | {c[n] / mf:.3g} | {n} / SQ_INSTS_MFMA |")
+            if all(n in c for n in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS")):
+                tot = (c["SQ_INSTS_VALU"] - mf + c["SQ_INSTS_SALU"] + c["SQ_INSTS_LDS"]) / mf
+                out.append(f"| {name} | non-MFMA VALU + SALU + LDS per MFMA | {tot:.3g} | "
+                           f"(SQ_INSTS_VALU - SQ_INSTS_MFMA + SALU + LDS) / SQ_INSTS_MFMA |")
+        wc = c.get("SQ_WAVE_CYCLES")
+        if wc:
+            for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"):
+                if n in c:
+                    out.append(f"| {name} | {n}, share of wave time | {c[n] / wc:.1%} | "
+                               f"{n} / SQ_WAVE_CYCLES |")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            out.append(f"| {name} | bf16 MFMA flops | {c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g} | "
+                       f"SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 |")
+    return "\n".join(out)
+
+
 def bench_table(jsonl: str) -> str:
     """One markdown row per bench.py JSON line (as printed by bench.py)."""
-    out = ["| workload | KV | µs/step | graph µs/step | KV-read rate per step | split (events) µs "
-           "| split b2b µs | single pass µs/step | bound | split kernel achieved | of measured "
-           "| CPU oracle |",
+    out = ["| workload | KV | µs/step | step median (p10-p90) µs | KV-read rate per step "
+           "| split (events) µs | split b2b µs | single pass µs/step | bound "
+           "| split kernel achieved | of measured | CPU oracle |",
            "|" + "---|" * 12]
     with open(jsonl) as f:
         recs = [json.loads(ln) for ln in f if ln.startswith("{")]
     for r in recs:
         c, rf, cpu = r["config"], r["roofline"], r.get("cpu_baseline")
         kv = "e4m3" if "e4m3" in c["latent"] else ("nope" if "NoPE" in c["latent"] else "bf16")
+        if "values" in c:
+            kv += " (exp2-reference worst case)"
+        pc = r.get("step_us_percentiles") or {}
+        med = f"{pc['median']} ({pc['p10']}-{pc['p90']})" if pc else "—"
         fmt = lambda v: "—" if v is None else f"{v}"
         unit = rf["unit"]
         ach = f"{rf['achieved']} {unit} ({rf['frac']:.1%})"
         cpu_s = f"{cpu['value']:.4g} {cpu['unit']} on {cpu['cores']} threads" if cpu else "—"
         out.append(
-            f"| {c['workload']} | {kv} | {r['us_per_step']} | {fmt(r.get('us_per_step_graph_replay'))} "
+            f"| {c['workload']} | {kv} | {r['us_per_step']} | {med} "
             f"| {r['value']} GB/s ({r['kv_frac_of_hbm_peak']:.1%} of 8 TB/s) | {r['split_pass_us']} "
             f"| {r['split_kernel_us_back_to_back']} | {fmt(r.get('single_pass_us_per_step'))} "
             f"| {rf['bound']} | {ach} | {rf.get('frac_of_measured_peak', 0):.0%} | {cpu_s} |")
@@ -170,7 +231,12 @@ def main(argv):
         with open(dst, "w") as f:
             f.write(f"# Hardware counters\n\nCommands:\n\n```\n{cmd}\n```\n\n")
             f.write(f"Kernel sources hash: `{kernel_hash()}`\n\n")
-            f.write(counters_table(argv[3:]) + "\n")
+            f.write(counters_table(argv[3:]) + "\n\n")
+            f.write("Derived figures.  Normalisation: GRBM_GUI_ACTIVE sums the 8 XCDs; "
+                    "SQ_VALU_MFMA_BUSY_CYCLES sums the 1,024 SIMDs, in cycles; SQ_WAVE_CYCLES, "
+                    "SQ_WAIT_* and SQ_ACTIVE_INST_* sum the resident waves, in units of 4 "
+                    "cycles; SQ_INSTS_VALU counts the MFMA instructions too.\n\n")
+            f.write(derived_table(argv[3:]) + "\n")
         print(dst)
     elif len(argv) >= 4 and argv[0] == "table":
         src, dst, cmd = argv[1], argv[2], argv[3]
