@@ -13,8 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_api.hip", "mla_kernels.hip", "mla_splitkv8.hip", "mla_append.hip",
-           "mla_project.hip"]
+SOURCES = ["mla_api.hip", "mla_kernels.hip", "mla_splitkv8.hip", "mla_splitkvq.hip",
+           "mla_append.hip", "mla_project.hip"]
 # the achievable-peak microbenchmarks the benchmark measures its denominators with
 PEAKS_LIB = os.path.join(PKG, "libmla_peaks.so")
 PEAKS_SOURCES = ["mla_peaks.hip"]

@@ -206,15 +206,17 @@ int prepare(const uint16_t* q_nope, const uint16_t* q_rope, const void* kv_pool,
   return MLA_OK;
 }
 
-// Which split-KV kernel runs a call: the eight-wave one where it applies (bf16 pools
-// without draft trees, two-pass calls) and is chosen, else the four-wave one.
-// MLA_SPLITKV=4 or =8 in the environment forces the choice where both apply.
-bool use_splitkv8(const SplitArgs& a) {
-  if (a.kv_e4m3 || a.kv_nope || a.tree_mask || a.arrive || a.wg_trace) return false;
+// Which split-KV kernel runs a call.  The quarter-split and eight-wave kernels apply to
+// bf16 pools without draft trees in two-pass calls; elsewhere the four-wave kernel
+// runs.  MLA_SPLITKV=4, =8 or =q in the environment forces the choice where it applies.
+enum class SplitKernel { kFour, kEight, kQuarter };
+
+SplitKernel split_kernel_for(const SplitArgs& a) {
+  if (a.kv_e4m3 || a.kv_nope || a.tree_mask || a.arrive || a.wg_trace) return SplitKernel::kFour;
   const char* v = getenv("MLA_SPLITKV");
-  if (v && v[0] == '8' && v[1] == 0) return true;
-  if (v && v[0] == '4' && v[1] == 0) return false;
-  return false;
+  if (v && v[0] == '8' && v[1] == 0) return SplitKernel::kEight;
+  if (v && v[0] == 'q' && v[1] == 0) return SplitKernel::kQuarter;
+  return SplitKernel::kFour;
 }
 
 int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
@@ -274,7 +276,12 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
     if (launch_clear_words(c.lay.arrive, 2 * (int64_t)B * c.geo.n_mt, stream) != hipSuccess)
       return MLA_ERR_HIP;
   }
-  const hipError_t e = use_splitkv8(a) ? launch_splitkv8(a, stream) : launch_splitkv(a, stream);
+  hipError_t e;
+  switch (split_kernel_for(a)) {
+    case SplitKernel::kEight: e = launch_splitkv8(a, stream); break;
+    case SplitKernel::kQuarter: e = launch_splitkvq(a, stream); break;
+    default: e = launch_splitkv(a, stream); break;
+  }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

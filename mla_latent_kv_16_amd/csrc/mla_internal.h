@@ -90,6 +90,7 @@ hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);
 // The same pass with eight waves per workgroup (bf16 pools, causal or full masks,
 // optional per-request draft counts; no trees, no single pass).
 hipError_t launch_splitkv8(const SplitArgs& a, hipStream_t stream);
+hipError_t launch_splitkvq(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t stream);
 

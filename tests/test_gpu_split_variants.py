@@ -1,6 +1,10 @@
-"""GPU parity of the eight-wave split-KV kernel (two waves per SIMD), which the
-library runs for bf16 pools when MLA_SPLITKV=8 is set (default: the four-wave kernel,
-measured faster on every configuration).  Same bar as tests/test_gpu_parity.py."""
+"""GPU parity of the optional split-KV kernels for bf16 pools, which the library runs
+when MLA_SPLITKV selects them (default: the four-wave kernel):
+  8  eight waves, two per SIMD: each wave 32 query rows and a quarter of the
+     contraction and of the output columns;
+  q  four waves, each holding the whole 64-row M-tile with a quarter of the
+     contraction and of the output columns.
+Same bar as tests/test_gpu_parity.py."""
 import math
 import os
 import sys
@@ -18,17 +22,18 @@ pytestmark = pytest.mark.gpu
 
 
 def say(*a):
-    print("[gpu-splitkv8]", *a, flush=True)
+    print("[gpu-split-variant]", *a, flush=True)
     sys.stdout.flush()
 
 
-@pytest.fixture(autouse=True)
-def _eight_waves(monkeypatch):
+@pytest.fixture(autouse=True, params=["8", "q"], ids=["eight-wave", "quarter"])
+def _variant(request, monkeypatch):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     if not os.path.exists(mla.LIB_PATH):
         pytest.fail("libmla.so is not built")
-    monkeypatch.setenv("MLA_SPLITKV", "8")
+    monkeypatch.setenv("MLA_SPLITKV", request.param)
+    say(f"MLA_SPLITKV={request.param}")
 
 
 def run(w, parts=0, fn=None):
