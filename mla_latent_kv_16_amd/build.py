@@ -39,11 +39,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; ROCm is required to build libmla.so")
 
 
+# libmla.so again with its host code under AddressSanitizer (the device code is the
+# same), for the CPU tests of the C ABI's host-side checks; the ASan runtime is loaded
+# by the test process, not linked in
+HOSTCHECK_LIB = os.path.join(PKG, "libmla_hostcheck.so")
+HOSTCHECK_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-shared-libasan"]
+
+
 def build(verbose: bool = True, extra=()) -> str:
-    """Compiles libmla.so (the attention path) and libmla_peaks.so (the peak
-    microbenchmarks) next to this file; returns the path of libmla.so."""
+    """Compiles libmla.so (the attention path), libmla_peaks.so (the peak
+    microbenchmarks) and libmla_hostcheck.so (libmla.so with AddressSanitizer on its
+    host code) next to this file; returns the path of libmla.so."""
     _build_one(PEAKS_LIB, PEAKS_SOURCES, verbose, extra)
+    _build_one(HOSTCHECK_LIB, SOURCES, verbose, [*extra, *HOSTCHECK_FLAGS])
     return _build_one(LIB, SOURCES, verbose, extra)
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (for LD_PRELOAD)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime of hipcc's clang was not found")
+    return path
 
 
 def _build_one(lib: str, sources, verbose: bool, extra) -> str:
