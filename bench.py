@@ -215,6 +215,44 @@ class DeviceWorkload:
         return int(self.seq_lens.astype("int64").sum()) * 1152
 
 
+def timeline_summary(torch, np, mla, hw, G, reps):
+    """Per-workgroup timelines of the split pass (mla_decode_splitkv_timeline) over
+    `reps` launches, each on the next pool copy: medians of the start-up phases, and per
+    XCD (the hardware XCC id each workgroup ran on) the median and latest end of the
+    walk and the latest completed stores, in us from the launch's first start."""
+    per_xcd = {x: {"walk_end_med": [], "walk_end_max": [], "stores_done_max": []} for x in range(8)}
+    phases = {"start_to_prefix": [], "prefix_to_first_block": [], "first_block_to_walk_end": [],
+              "walk_end_to_stores_done": []}
+    spans = []
+    for r in range(reps):
+        pool = hw.pools[r % len(hw.pools)]
+        _, _, trace, ticks = mla.decode_splitkv_timeline(
+            hw.q_nope, hw.q_rope, pool, hw.bt, hw.sl, hw.scale, causal=hw.causal,
+            num_partitions=G)
+        torch.cuda.synchronize()
+        tr, tk = trace.cpu().numpy(), ticks.cpu().numpy().astype(np.float64)
+        tk = tk[(tk > 0).all(axis=1)]
+        xcc = tr[(ticks.cpu().numpy() > 0).all(axis=1), 0]
+        us = (tk - tk[:, 0].min()) / 100.0
+        spans.append(float(us[:, 4].max()))
+        d = np.diff(us, axis=1)
+        for k, name in enumerate(phases):
+            phases[name].append(float(np.median(d[:, k])))
+        for x in range(8):
+            m = xcc == x
+            if m.any():
+                per_xcd[x]["walk_end_med"].append(float(np.median(us[m, 3])))
+                per_xcd[x]["walk_end_max"].append(float(us[m, 3].max()))
+                per_xcd[x]["stores_done_max"].append(float(us[m, 4].max()))
+    med = lambda v: round(float(np.median(v)), 2) if v else None
+    return {"launches": reps, "span_us_median": med(spans),
+            "phase_us_median": {k: med(v) for k, v in phases.items()},
+            "per_xcd": [{"xcc": x, **{k: [round(a, 2) for a in v] for k, v in per_xcd[x].items()}}
+                        for x in range(8)],
+            "how": "mla_decode_splitkv_timeline: 100 MHz clock stamps per workgroup (start, "
+                   "page prefix, first block in LDS, walk over, stores complete) and its XCC id"}
+
+
 def roofline(work, kernel_s, traffic):
     """The dominant kernel against the roof the step's arithmetic intensity meets first."""
     hbm = work["bytes"] / kernel_s / 1e9
@@ -356,6 +394,9 @@ def main():
                          "on scaled by 8 and queries drawn N(0, 4^2), so that later scores pass "
                          "the first block's reference by far more than 32 (log2) and each piece is "
                          "walked three times (bf16 pools)")
+    ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
+                    help="after timing, record per-workgroup timelines of this many split "
+                         "passes (bf16 pools) and add their per-XCD summary to the line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, launch a plain 256 MiB device copy 3 times (counter "
                          "calibration for rocprofv3 --pmc runs)")
@@ -417,6 +458,13 @@ def main():
         single_pass_us = (time.perf_counter() - t0) * 1e6 / args.steps
         if mla.read_error_flags(ws):
             raise SystemExit("kernel reported a data fault flag")
+
+    timeline = None
+    if args.timeline:
+        if args.kv != "bf16" or args.nope:
+            raise SystemExit("--timeline takes bf16 pools")
+        timeline = timeline_summary(torch, np, mla, hw, G, args.timeline)
+        log(f"timeline: {json.dumps(timeline)}")
 
     if args.copy_probe:
         from mla_latent_kv_16_amd.profiling import COPY_PROBE_BYTES
@@ -538,6 +586,7 @@ def main():
                            else round(append_bytes / (append_us * 1e-6) / 1e9, 2)),
         "absorb_project": gemm or None,
         "measured_peaks": peaks,
+        **({"timeline": timeline} if timeline else {}),
         "sub_records": subs or None,
         "cpu_baseline": cpu,
     }

@@ -240,6 +240,31 @@ int mla_decode_splitkv_placement(const uint16_t* q_nope, const uint16_t* q_rope,
                                  int32_t* wg_trace, int64_t wg_trace_len, void* stream);
 
 /*
+ * The placement record plus a timeline of every split-KV workgroup, for measuring
+ * where a split pass spends its time on the device at hand (start-up round trips, the
+ * stream, the end skew between XCDs; "Faster kernels, slower engine", §7.1 on how
+ * close a decode kernel's loads get to peak bandwidth).
+ *   wg_trace, wg_trace_len  as for mla_decode_splitkv_placement
+ *   wg_time       int64 device buffer, 8-byte aligned; workgroup w writes ticks of the
+ *                 GPU's 100 MHz constant clock to wg_time[5 w .. 5 w + 4]: its start,
+ *                 the batch's page prefix built, the first block of its last piece in
+ *                 LDS, the end of that piece's walk, and all of its stores complete.
+ *                 A workgroup whose partition holds no page writes only the first two.
+ *   wg_time_len   entries available; fewer than 5 per workgroup -> MLA_ERR_INVALID_ARG
+ *                 (as is a NULL or misaligned wg_time), before anything is enqueued
+ * Every other argument, and O, lse and the workspace contents, exactly as for
+ * mla_decode_splitkv (the records change no result).
+ */
+int mla_decode_splitkv_timeline(const uint16_t* q_nope, const uint16_t* q_rope,
+                                const uint16_t* kv_pool, int64_t num_pages, int page_size,
+                                const int32_t* block_table, int max_pages_per_seq,
+                                const int32_t* seq_lens, int B, int Sq, int H,
+                                float softmax_scale, int causal, int num_partitions, float* O,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                int32_t* wg_trace, int64_t wg_trace_len, int64_t* wg_time,
+                                int64_t wg_time_len, void* stream);
+
+/*
  * Chunked prefill on top of a long cached prefix (atlas §11 Chunked prefill;
  * TokenSpeed launch news, prefill-kernel paragraph).  Sq is the chunk length,
  * seq_lens[b] = cached prefix + chunk, and the chunk's own latent rows are already

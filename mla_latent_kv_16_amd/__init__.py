@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     decode_single_pass_e4m3,
     decode_splitkv,
     decode_splitkv_placement,
+    decode_splitkv_timeline,
     decode_splitkv_e4m3,
     decode_tree,
     decode_varlen,

@@ -70,6 +70,7 @@ _SIGNATURES = {
     "mla_decode_splitkv_e4m3": (_COMPUTE_ARGS_E4M3, _i32),
     "mla_decode_combine": ([_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "mla_decode_splitkv_placement": (_COMPUTE_ARGS[:-1] + [_vp, _i64, _vp], _i32),
+    "mla_decode_splitkv_timeline": (_COMPUTE_ARGS[:-1] + [_vp, _i64, _vp, _i64, _vp], _i32),
     "mla_read_error_flags": ([_vp, _vp, ctypes.POINTER(ctypes.c_uint32)], _i32),
 }
 
@@ -474,6 +475,30 @@ def decode_splitkv_placement(q_nope, q_rope, kv_pool, block_table, seq_lens, sof
         workspace.numel(), _ptr(trace), trace.numel(), _stream_handle(stream))
     _check(st, "mla_decode_splitkv_placement")
     return out, lse, trace
+
+
+def decode_splitkv_timeline(q_nope, q_rope, kv_pool, block_table, seq_lens, softmax_scale,
+                            causal=True, num_partitions=0, out=None, lse=None, workspace=None,
+                            stream=None):
+    """mla_decode_splitkv_timeline: the split-KV pass plus, per split-KV workgroup in
+    launch order, the (XCC id, KV partition, M-tile) it ran with (int32 [n, 3]) and five
+    ticks of the 100 MHz constant clock (int64 [n, 5]: start, page prefix built, first
+    block in LDS, walk over, stores complete; 0 where not reached)."""
+    torch = _torch()
+    B, Sq, H, maxp, out, lse, workspace = _prep(q_nope, q_rope, kv_pool, block_table, seq_lens,
+                                                out, lse, workspace, num_partitions)
+    G = int(num_partitions) or auto_partitions(B, Sq, H, maxp)
+    n_wg = G * ((Sq * H + 63) // 64)
+    trace = torch.full((n_wg, 3), -1, dtype=torch.int32, device=q_nope.device)
+    ticks = torch.zeros((n_wg, 5), dtype=torch.int64, device=q_nope.device)
+    st = lib().mla_decode_splitkv_timeline(
+        _ptr(q_nope), _ptr(q_rope), _ptr(kv_pool), kv_pool.shape[0], PAGE_SIZE,
+        _ptr(block_table), maxp, _ptr(seq_lens), B, Sq, H, float(softmax_scale),
+        1 if causal else 0, int(num_partitions), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _ptr(trace), trace.numel(), _ptr(ticks), ticks.numel(),
+        _stream_handle(stream))
+    _check(st, "mla_decode_splitkv_timeline")
+    return out, lse, trace, ticks
 
 
 def decode_combine(seq_lens, max_pages_per_seq, Sq, H, out, lse, workspace, num_partitions=0,

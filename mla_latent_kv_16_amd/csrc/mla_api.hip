@@ -224,9 +224,11 @@ int enqueue_split(const Call& c, const uint16_t* q_nope, const uint16_t* q_rope,
                   const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                   const uint64_t* tree_mask, int B, int Sq, int H, float scale, int causal,
                   float* O, float* lse, bool single_pass, hipStream_t stream,
-                  const int32_t* q_lens = nullptr, int32_t* wg_trace = nullptr) {
+                  const int32_t* q_lens = nullptr, int32_t* wg_trace = nullptr,
+                  int64_t* wg_time = nullptr) {
   SplitArgs a;
   a.wg_trace = wg_trace;
+  a.wg_time = wg_time;
   a.tree_mask = tree_mask;
   a.q_lens = q_lens;
   a.len_min = q_lens ? 1 : Sq;
@@ -452,6 +454,31 @@ int mla_decode_splitkv_placement(const uint16_t* q_nope, const uint16_t* q_rope,
                               block_table, max_pages_per_seq, seq_lens, nullptr, B, Sq, H,
                               softmax_scale, causal, O, lse, false,
                               static_cast<hipStream_t>(stream), nullptr, wg_trace),
+                workspace, static_cast<hipStream_t>(stream));
+}
+
+int mla_decode_splitkv_timeline(const uint16_t* q_nope, const uint16_t* q_rope,
+                                const uint16_t* kv_pool, int64_t num_pages, int page_size,
+                                const int32_t* block_table, int max_pages_per_seq,
+                                const int32_t* seq_lens, int B, int Sq, int H,
+                                float softmax_scale, int causal, int num_partitions, float* O,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                int32_t* wg_trace, int64_t wg_trace_len, int64_t* wg_time,
+                                int64_t wg_time_len, void* stream) {
+  Call c;
+  int st = prepare(q_nope, q_rope, kv_pool, num_pages, page_size, block_table, max_pages_per_seq,
+                   seq_lens, B, Sq, H, softmax_scale, causal, num_partitions, O, lse, workspace,
+                   workspace_bytes, &c);
+  if (st != MLA_OK) return st;
+  const int64_t nwg = (int64_t)c.G * c.geo.n_mt;
+  if (!wg_trace || (reinterpret_cast<uintptr_t>(wg_trace) & 3)) return MLA_ERR_INVALID_ARG;
+  if (wg_trace_len < 3 * nwg) return MLA_ERR_INVALID_ARG;
+  if (!wg_time || (reinterpret_cast<uintptr_t>(wg_time) & 7)) return MLA_ERR_INVALID_ARG;
+  if (wg_time_len < 5 * nwg) return MLA_ERR_INVALID_ARG;
+  return finish(enqueue_split(c, q_nope, q_rope, kv_pool, kFormatBf16, 1.0f, num_pages,
+                              block_table, max_pages_per_seq, seq_lens, nullptr, B, Sq, H,
+                              softmax_scale, causal, O, lse, false,
+                              static_cast<hipStream_t>(stream), nullptr, wg_trace, wg_time),
                 workspace, static_cast<hipStream_t>(stream));
 }
 

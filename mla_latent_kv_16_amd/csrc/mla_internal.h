@@ -44,6 +44,11 @@ struct SplitArgs {
   // Placement record (or nullptr): split-KV workgroup w writes its XCD (the hardware
   // XCC id), partition and M-tile to wg_trace[3 w .. 3 w + 2].
   int32_t* wg_trace;           // [n_split, 3]
+  // Timeline record (or nullptr; only with a placement record): split-KV workgroup w
+  // writes ticks of the 100 MHz constant clock to wg_time[5 w .. 5 w + 4]: its start,
+  // the page prefix built, the first block of its last piece landed, the end of that
+  // piece's walk, and every store of the workgroup complete.
+  int64_t* wg_time;            // [n_split, 5]
 };
 
 struct CombineArgs {

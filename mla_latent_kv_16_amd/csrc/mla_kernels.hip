@@ -935,6 +935,8 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     }
     wait_copy_sets<Kv::kCopies, AHEAD - 1>(min(nb, AHEAD) - 1);  // block 0 has landed
     __syncthreads();
+    if (a.wg_time && threadIdx.x == 0 && pass == (Kv::kLazyMax ? 0 : 1))  // block 0 is in LDS
+      a.wg_time[5 * (size_t)blockIdx.x + 2] = (int64_t)wall_clock64();
     f32x16 s_own = {};  // this wave's half of S^T of the block being scored
     if (nb > 0) {
       s_own = qk_partial<Kv>(ring_slot<Kv>(ring, 0), rb, qreg);
@@ -985,6 +987,8 @@ __device__ __forceinline__ void run_piece(const SplitArgs& a, uint8_t* ring, f32
     if (!redo) break;
   }
 
+  if (a.wg_time && threadIdx.x == 0)  // the walk (and any re-walk) is over
+    a.wg_time[5 * (size_t)blockIdx.x + 3] = (int64_t)wall_clock64();
   // the pair's weight sums: each wave summed the weights of its own k-step of P.  Both
   // waves add them in the same order (the C = 0 wave's first), so both normalise their
   // columns by the same sums.
@@ -1335,6 +1339,8 @@ splitkv_kernel(SplitArgs a) {
                           : a.n_split - 1 - (int)blockIdx.x;
   const int g = lam / a.n_mt;
   const int mt = lam - g * a.n_mt;
+  int64_t* tl = a.wg_time ? a.wg_time + 5 * (size_t)blockIdx.x : nullptr;
+  if (tl && threadIdx.x == 0) tl[0] = (int64_t)wall_clock64();
   if (a.wg_trace && threadIdx.x == 0) {
     // where this workgroup actually runs: the XCC id register of the executing die
     uint32_t xcc;
@@ -1350,6 +1356,7 @@ splitkv_kernel(SplitArgs a) {
   int* prefix = reinterpret_cast<int*>(xbuf);
   int* lens = prefix + kMaxBatch + 1;
   build_page_prefix(a.seq_lens, a.B, a.len_min, a.max_pages, prefix, a.flags, true, lens);
+  if (tl && threadIdx.x == 0) tl[1] = (int64_t)wall_clock64();
   if (a.q_lens && threadIdx.x < 64) {  // per-request draft counts outside [1, min(Sq, L_b)]
     for (int j = threadIdx.x; j < a.B; j += 64) {
       const int q = a.q_lens[j];
@@ -1405,6 +1412,11 @@ splitkv_kernel(SplitArgs a) {
       __syncthreads();  // LDS free before the next piece stages into it
     }
     pb0 = pb1;
+  }
+  if (tl) {  // every store of the workgroup is complete
+    wait_vmem_all();
+    __syncthreads();
+    if (threadIdx.x == 0) tl[4] = (int64_t)wall_clock64();
   }
 }
 

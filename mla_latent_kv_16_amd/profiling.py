@@ -5,6 +5,7 @@
                                                      <workload> <out.json> "<commands>"
     python -m mla_latent_kv_16_amd.profiling counters <out.md> "<commands>" <counter.csv>...
     python -m mla_latent_kv_16_amd.profiling table    <bench.jsonl> <out.md> "<commands>"
+    python -m mla_latent_kv_16_amd.profiling timeline <bench.jsonl> <out.md> "<command>"
 
 `stats` keeps the per-kernel table of a `--kernel-trace --stats` run.  `traffic`
 turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of `bench.py --copy-probe`
@@ -213,6 +214,32 @@ def bench_table(jsonl: str) -> str:
     return "\n".join(out)
 
 
+def timeline_table(jsonl: str) -> str:
+    """Markdown of the `timeline` object of each bench.py JSON line that has one."""
+    out = []
+    with open(jsonl) as f:
+        recs = [json.loads(ln) for ln in f if ln.startswith("{")]
+    for r in recs:
+        t = r.get("timeline")
+        if not t:
+            continue
+        c = r["config"]
+        out.append(f"## {c['workload']} (B={c['B']}, Sq={c['Sq']}, H={c['H']}, "
+                   f"partitions={c['partitions']}), {t['launches']} launches\n")
+        out.append(f"Median span of a launch (first start to last stores): {t['span_us_median']} us\n")
+        out.append("| phase (median over workgroups, then over launches) | us |\n|---|---|")
+        for k, v in t["phase_us_median"].items():
+            out.append(f"| {k.replace('_', ' ')} | {v} |")
+        out.append("\n| XCC | walk end, median (per launch) | walk end, latest | stores done, "
+                   "latest |\n|---|---|---|---|")
+        for x in t["per_xcd"]:
+            fmt = lambda v: ", ".join(f"{a:.1f}" for a in v)
+            out.append(f"| {x['xcc']} | {fmt(x['walk_end_med'])} | {fmt(x['walk_end_max'])} | "
+                       f"{fmt(x['stores_done_max'])} |")
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         src, dst, cmd = argv[1], argv[2], argv[3]
@@ -237,6 +264,14 @@ def main(argv):
                     "SQ_WAIT_* and SQ_ACTIVE_INST_* sum the resident waves, in units of 4 "
                     "cycles; SQ_INSTS_VALU counts the MFMA instructions too.\n\n")
             f.write(derived_table(argv[3:]) + "\n")
+        print(dst)
+    elif len(argv) >= 4 and argv[0] == "timeline":
+        src, dst, cmd = argv[1], argv[2], argv[3]
+        with open(dst, "w") as f:
+            f.write(f"# Split-pass timelines per workgroup and XCD\n\nCommand:\n\n```\n{cmd}\n```\n\n"
+                    f"Kernel sources hash: `{kernel_hash()}`\n\nTimes in us from the "
+                    f"launch's first workgroup start (100 MHz constant clock).\n\n")
+            f.write(timeline_table(src) + "\n")
         print(dst)
     elif len(argv) >= 4 and argv[0] == "table":
         src, dst, cmd = argv[1], argv[2], argv[3]

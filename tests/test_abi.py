@@ -25,7 +25,8 @@ def test_library_exports_every_header_function():
         "mla_decode", "mla_decode_auto_partitions", "mla_decode_combine", "mla_decode_e4m3",
         "mla_decode_nope", "mla_decode_noalloc", "mla_decode_splitkv_nope",
         "mla_decode_single_pass", "mla_decode_single_pass_e4m3", "mla_decode_splitkv",
-        "mla_decode_splitkv_e4m3", "mla_decode_splitkv_placement", "mla_decode_tree",
+        "mla_decode_splitkv_e4m3", "mla_decode_splitkv_placement",
+        "mla_decode_splitkv_timeline", "mla_decode_tree",
         "mla_decode_tree_e4m3",
         "mla_decode_varlen", "mla_decode_workspace_bytes", "mla_decode_workspace_size",
         "mla_kv_append", "mla_kv_append_e4m3", "mla_prefill_with_prefix",
@@ -283,6 +284,24 @@ def test_placement_record_rejects_on_host():
     assert call(FAKE, 3 * 32, parts=-1) == INVALID
     assert call(FAKE, 3 * 32, B=0) == INVALID
     assert call(FAKE, 3 * 8 - 1, Sq=4, parts=8) == INVALID  # one M-tile: 8 workgroups
+
+
+def test_timeline_records_reject_on_host():
+    """The timeline needs the placement record (3 int32 per split-KV workgroup) and 5
+    int64 per workgroup in an 8-byte-aligned buffer; any shortfall is refused before
+    anything is enqueued."""
+    f = mla.lib().mla_decode_splitkv_timeline
+
+    def call(trace, n, times, m, parts=8):
+        return f(FAKE, FAKE, FAKE, 64, 64, FAKE, 16, FAKE, 4, 16, 16, 0.07, 1, parts, FAKE, FAKE,
+                 FAKE, 1 << 30, trace, n, times, m, None)
+    # 4 M-tiles x 8 partitions = 32 workgroups
+    assert call(FAKE, 3 * 32 - 1, FAKE, 5 * 32) == INVALID
+    assert call(FAKE, 3 * 32, FAKE, 5 * 32 - 1) == INVALID
+    assert call(FAKE, 3 * 32, None, 5 * 32) == INVALID
+    assert call(FAKE, 3 * 32, FAKE + 4, 5 * 32) == INVALID
+    assert call(None, 3 * 32, FAKE, 5 * 32) == INVALID
+    assert call(FAKE, 3 * 32, FAKE, 5 * 32, parts=-1) == INVALID
 
 
 def test_read_error_flags_rejects_null():

@@ -127,3 +127,38 @@ def test_placement_record_changes_no_result():
     torch.cuda.synchronize()
     assert torch.equal(O, O2) and torch.equal(lse, lse2)
     assert torch.equal(ws, ws2)
+
+
+def test_timeline_is_ordered_and_changes_no_result():
+    """The timeline record: every workgroup with pages stamps start <= page prefix <=
+    first block <= walk over <= stores complete, on one clock, within the launch; the
+    placement part matches the placement record; results are bitwise those of the
+    plain split pass."""
+    w = make_workload("tiny", seed=706, B=4, Sq=4, H=16, lens=("uniform", 2000, 5000))
+    parts = 64
+    args = dev_inputs(w)
+    say(f"timeline B={w.B} Sq={w.Sq} H={w.H} parts={parts}")
+    O = torch.zeros((w.B, w.Sq, w.H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((w.B, w.Sq, w.H), dtype=torch.float32, device="cuda")
+    ws = mla.new_workspace(w.B, w.Sq, w.H, w.block_table.shape[1], parts)
+    _, _, trace, ticks = mla.decode_splitkv_timeline(*args, float(w.scale), causal=True,
+                                                     num_partitions=parts, out=O, lse=lse,
+                                                     workspace=ws)
+    torch.cuda.synchronize()
+    tr, tk = trace.cpu().numpy(), ticks.cpu().numpy()
+    n = parts  # one M-tile
+    assert tr.shape == (n, 3) and tk.shape == (n, 5)
+    assert sorted(tr[:, 1].tolist()) == list(range(parts))
+    assert ((tr[:, 0] >= 0) & (tr[:, 0] < XCDS)).all()
+    assert (tk > 0).all(), "every partition holds pages here, so every stamp is written"
+    assert (np.diff(tk, axis=1) >= 0).all(), "stamps out of order"
+    span_us = (tk[:, 4].max() - tk[:, 0].min()) / 100.0
+    assert 0 < span_us < 1e6, span_us
+    O2 = torch.zeros_like(O)
+    lse2 = torch.zeros_like(lse)
+    ws2 = mla.new_workspace(w.B, w.Sq, w.H, w.block_table.shape[1], parts)
+    mla.decode_splitkv(*args, float(w.scale), causal=True, num_partitions=parts, out=O2,
+                       lse=lse2, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(lse, lse2)
+    say(f"timeline: {n} workgroups over {span_us:.1f} us")
