@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdlib.h>
 #include <mutex>
+#include <numeric>
 
 namespace {
 
@@ -62,16 +63,21 @@ int geometry(int B, int Sq, int H, int max_pages, Geometry* g) {
 // evenly; below four pages per partition a candidate must also divide the page count,
 // since a partition that straddles two requests walks and writes two pieces.  The
 // page count is the block table's capacity, an upper bound of the real one.
-int auto_partitions(const Geometry& g, int B, int max_pages, int cus) {
+//
+// One refinement from the same measurements: with one M-tile per request and walks of
+// 8 to 32 pages per workgroup, about 80% of the compute units already keep the HBM
+// stream of the pages saturated, and the remaining partitions only add partials and
+// merge work.  There the count is capped at about 80% of the compute units, rounded
+// up to a multiple of B and of the eight XCDs (a spec-decode step of B = 4, Sq = 4,
+// 65,540 rows: 75.7 us at 208 partitions against 79.5 us at 256, and 208 ahead of 204
+// and 200, which leave the XCDs uneven; 32,772 rows: 47.0 against 49.7 us).  Longer walks (64 pages per workgroup:
+// 232.6 us at 256 against 238.9 at 224) and shorter ones keep the plain model.  The
+// cap does not depend on the pool format; E4M3 pools, whose walk is bound by the
+// widening VALU rather than by HBM, would keep every compute unit (72.5 against
+// 76.2 us at 208), but one count per shape keeps the split and combine calls of every
+// format in step.
+int pick_partitions(const Geometry& g, int B, int64_t pages, int64_t gmax) {
   constexpr double kUsPerPage = 2.8, kUsPerPartialMB = 0.44, kUsMerge = 4.0;
-  const int64_t pages = (int64_t)B * max_pages;
-  int64_t gmax = cus / g.n_mt;
-  if (gmax > pages) gmax = pages;
-  if (gmax < 1) gmax = 1;
-  if (B > gmax) {  // fewer partitions than requests: at least about four pages each
-    const int64_t by_pages = (pages + 3) / 4;
-    return (int)(by_pages < gmax ? by_pages : gmax);
-  }
   const double piece_mb = (double)g.n_mt * g.slot_rows * (kNope + 1) * 4 * 1e-6;
   int64_t best = 1;
   double best_us = (double)pages * kUsPerPage;
@@ -85,6 +91,25 @@ int auto_partitions(const Geometry& g, int B, int max_pages, int cus) {
     }
   }
   return (int)best;
+}
+
+int auto_partitions(const Geometry& g, int B, int max_pages, int cus) {
+  const int64_t pages = (int64_t)B * max_pages;
+  int64_t gmax = cus / g.n_mt;
+  if (gmax > pages) gmax = pages;
+  if (gmax < 1) gmax = 1;
+  if (B > gmax) {  // fewer partitions than requests: at least about four pages each
+    const int64_t by_pages = (pages + 3) / 4;
+    return (int)(by_pages < gmax ? by_pages : gmax);
+  }
+  const int best = pick_partitions(g, B, pages, gmax);
+  // 80% of the CUs, rounded up to a multiple of both B and the eight XCDs, so that the
+  // requests split evenly and every XCD runs as many workgroups as the others
+  const int64_t unit = std::lcm((int64_t)B, (int64_t)8);
+  const int64_t cap = ((int64_t)cus * 4 / 5 + unit - 1) / unit * unit;
+  if (g.n_mt == 1 && best > cap && pages >= 8 * (int64_t)best && pages <= 32 * (int64_t)best)
+    return pick_partitions(g, B, pages, cap);
+  return best;
 }
 
 int resolve_partitions(const Geometry& g, int B, int max_pages, int requested, int* G) {

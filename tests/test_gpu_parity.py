@@ -282,9 +282,13 @@ def test_maximum_batch(parts, single):
 
 
 # default partition counts (256 CUs): the long-context decode shapes take one
-# (partition x M-tile) workgroup per CU, prefill none, and short contexts the count
-# the cost model picks (each measured faster than the old four-pages floor, or equal)
-AUTO_G = [((1, 1, 16, 4), 4), ((4, 4, 16, 1025), 256), ((8, 8, 16, 2049), 128),
+# (partition x M-tile) workgroup per CU, except one M-tile per request with 8 to 32
+# pages per workgroup (80% of the CUs, rounded up to a multiple of B and of 8: 208 at
+# spec4), prefill none, and short contexts
+# the count the cost model picks (each measured faster than the old four-pages floor,
+# or equal)
+AUTO_G = [((1, 1, 16, 4), 4), ((4, 4, 16, 1025), 208), ((8, 8, 16, 2049), 128),
+          ((4, 4, 16, 513), 208), ((16, 4, 16, 1024), 256), ((2, 4, 16, 1025), 208),
           ((16, 16, 16, 3201), 64), ((64, 1, 128, 512), 128), ((1, 4096, 16, 1088), 1),
           ((1, 4, 16, 16), 16), ((4, 4, 16, 16), 64), ((16, 1, 16, 32), 256),
           ((4, 4, 16, 32), 64), ((4, 4, 16, 128), 128), ((300, 1, 16, 10), 256)]
