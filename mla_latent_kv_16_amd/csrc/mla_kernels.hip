@@ -1073,16 +1073,20 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // Many pieces per request (G >= 16 B): one workgroup merges folded query row `row`
-// = (b, m).  Thread t handles columns 8 (t % 64) .. + 8 of the pieces s with
-// s % 4 == t / 64.  The partial outputs of a chunk of 64 pieces (16 per thread) are
-// all requested at once, before the row's log-sum-exp over the pieces is reduced,
-// so that one memory round trip covers both; the four piece lanes are summed
-// through LDS.  prefix: kMaxBatch + 1 ints, red: 4 floats, part: 4 x 512 floats.
+// = (b, m), all 512 columns (half < 0) or one half of them (half = 0 or 1; the
+// separate combine kernel runs two workgroups per row).  Thread t handles the pieces
+// s with s % 4 == t / 64 and the four-column groups 4 (t % 64) and 256 + 4 (t % 64)
+// (only the one in its half when half >= 0), so that each load instruction of a wave
+// reads 1 KB of one partial row contiguously.  The partial outputs of a chunk of 64
+// pieces (16 per thread) are all requested at once, before the row's log-sum-exp over
+// the pieces is reduced, so that one memory round trip covers both; the four piece
+// lanes are summed through LDS.  Every column is summed in the same order whatever
+// `half` is.  prefix: kMaxBatch + 1 ints, red: 4 floats, part: 4 x 512 floats.
 constexpr int kCombineLanes = kCombineThreads / 64;
 constexpr int kCombineChunk = 16;  // pieces per thread per chunk
 
 __device__ __forceinline__ void merge_row_group(const CombineArgs& a, int row, int* prefix,
-                                                float* red, float* part) {
+                                                float* red, float* part, int half = -1) {
   build_page_prefix(a.seq_lens, a.B, a.Sq, a.max_pages, prefix, a.flags, false);
   const int64_t T = prefix[a.B];
   const int b = row / a.M, m = row - b * a.M;
@@ -1118,7 +1122,8 @@ __device__ __forceinline__ void merge_row_group(const CombineArgs& a, int row, i
   const int cg = tid & 63, pl = tid >> 6;
   auto src_of = [&](int s) {
     const size_t slot = (size_t)(b + g0 + s) * a.n_mt + mt;
-    return a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * cg;
+    return a.part_o + (slot * a.slot_rows + ml) * kNope + 4 * cg +
+           (half > 0 ? kNope / 2 : 0);
   };
 
   f32x4 v0[kCombineChunk], v1[kCombineChunk];
@@ -1131,7 +1136,7 @@ __device__ __forceinline__ void merge_row_group(const CombineArgs& a, int row, i
       if (s < n) {
         const float* src = src_of(s);
         v0[u] = *reinterpret_cast<const f32x4*>(src);
-        v1[u] = *reinterpret_cast<const f32x4*>(src + 4);
+        if (half < 0) v1[u] = *reinterpret_cast<const f32x4*>(src + kNope / 2);
         lv[u] = lse_of(s);
       }
     }
@@ -1156,7 +1161,7 @@ __device__ __forceinline__ void merge_row_group(const CombineArgs& a, int row, i
       const float w = (seen && lv[u] != -INFINITY) ? exp2f(lv[u] - lse2) : 0.0f;
       // a zero-weight slot may hold stale data, even NaN: select, never multiply
       o0 = w != 0.0f ? o0 + w * v0[u] : o0;
-      o1 = w != 0.0f ? o1 + w * v1[u] : o1;
+      if (half < 0) o1 = w != 0.0f ? o1 + w * v1[u] : o1;
     }
   };
   accumulate();
@@ -1165,19 +1170,20 @@ __device__ __forceinline__ void merge_row_group(const CombineArgs& a, int row, i
     accumulate();
   }
 
-  *reinterpret_cast<f32x4*>(&part[pl * 512 + 8 * cg]) = o0;
-  *reinterpret_cast<f32x4*>(&part[pl * 512 + 8 * cg + 4]) = o1;
+  *reinterpret_cast<f32x4*>(&part[pl * 512 + 4 * cg]) = o0;
+  *reinterpret_cast<f32x4*>(&part[pl * 512 + 4 * cg + 256]) = o1;
   __syncthreads();
   if (pl == 0) {
 #pragma unroll
     for (int q = 1; q < kCombineLanes; ++q) {
-      o0 += *reinterpret_cast<const f32x4*>(&part[q * 512 + 8 * cg]);
-      o1 += *reinterpret_cast<const f32x4*>(&part[q * 512 + 8 * cg + 4]);
+      o0 += *reinterpret_cast<const f32x4*>(&part[q * 512 + 4 * cg]);
+      o1 += *reinterpret_cast<const f32x4*>(&part[q * 512 + 4 * cg + 256]);
     }
-    float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * cg;
+    float* dst = a.O + ((size_t)b * a.M + m) * kNope + 4 * cg +
+                 (half > 0 ? kNope / 2 : 0);
     *reinterpret_cast<f32x4*>(dst) = o0;
-    *reinterpret_cast<f32x4*>(dst + 4) = o1;
-    if (cg == 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
+    if (half < 0) *reinterpret_cast<f32x4*>(dst + kNope / 2) = o1;
+    if (cg == 0 && half <= 0) a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
   }
   if (a.arrive && tid == 0) row_merged(a, idx, mt);
 }
@@ -1185,8 +1191,9 @@ __device__ __forceinline__ void merge_row_group(const CombineArgs& a, int row, i
 // Few pieces per request: one wave merges folded query row `row`, with no LDS and no
 // barriers.  The wave finds its request's page range by summing the clamped page
 // counts itself, reduces the row's log-sum-exp over the pieces with lane shuffles,
-// and lane l accumulates columns 8 l .. 8 l + 7 over all pieces, four pieces' loads
-// in flight at a time.
+// and lane l accumulates columns 4 l .. 4 l + 3 and 256 + 4 l .. 256 + 4 l + 3 over
+// all pieces (each load instruction reads 1 KB of a partial row contiguously), four
+// pieces' loads in flight at a time.
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -1255,9 +1262,9 @@ __device__ __forceinline__ void merge_row_wave(const CombineArgs& a, int64_t row
       w[u] = 0.0f;
       if (s < n) {
         const size_t slot = (size_t)(b + g0 + s) * a.n_mt + mt;
-        const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + 8 * lane;
+        const float* src = a.part_o + (slot * a.slot_rows + ml) * kNope + 4 * lane;
         v0[u] = *reinterpret_cast<const f32x4*>(src);
-        v1[u] = *reinterpret_cast<const f32x4*>(src + 4);
+        v1[u] = *reinterpret_cast<const f32x4*>(src + kNope / 2);
         const float l = lse_of(s);
         w[u] = (seen && l != -INFINITY) ? exp2f(l - lse2) : 0.0f;
       }
@@ -1269,9 +1276,9 @@ __device__ __forceinline__ void merge_row_wave(const CombineArgs& a, int64_t row
       o1 = w[u] != 0.0f ? o1 + w[u] * v1[u] : o1;
     }
   }
-  float* dst = a.O + ((size_t)b * a.M + m) * kNope + 8 * lane;
+  float* dst = a.O + ((size_t)b * a.M + m) * kNope + 4 * lane;
   *reinterpret_cast<f32x4*>(dst) = o0;
-  *reinterpret_cast<f32x4*>(dst + 4) = o1;
+  *reinterpret_cast<f32x4*>(dst + kNope / 2) = o1;
   if (lane == 0) {
     a.lse[(size_t)b * a.M + m] = lse2 * kLn2;
     if (a.arrive) row_merged(a, idx, mt);
@@ -1421,11 +1428,12 @@ splitkv_kernel(SplitArgs a) {
 }
 
 // ---- the separate combine kernels (two-pass calls) ----------------------------------
+// two workgroups per row, one per half of the columns
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
   __shared__ int prefix[kMaxBatch + 1];
   __shared__ float red[kCombineLanes];
   __shared__ __attribute__((aligned(16))) float part[kCombineLanes * 512];
-  merge_row_group(a, blockIdx.x, prefix, red, part);
+  merge_row_group(a, blockIdx.x >> 1, prefix, red, part, blockIdx.x & 1);
 }
 
 // four rows per workgroup, one wave each
@@ -1474,9 +1482,11 @@ hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t stream) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.M;
   if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidValue;
-  // about G / B pieces per request: spread many over a workgroup, few over a wave
+  // about G / B pieces per request: spread many over two workgroups, few over a wave
   if ((int64_t)a.G >= 16 * (int64_t)a.B) {
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, a);
+    if (rows > 0x3fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(2 * rows)), dim3(kCombineThreads), 0,
+                       stream, a);
   } else {
     const int64_t groups = (rows + kRowsPerCombineGroup - 1) / kRowsPerCombineGroup;
     hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)groups), dim3(kCombineThreads), 0,
