@@ -26,10 +26,19 @@ decode configurations of the metric (B=8 and B=16 spec-decode, the H=128 sweep)
 and the prefix prefill are timed too, each as a sub-record with its own roofline.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the main workload.
 
+Step counts: --steps K and --warmup W are taken exactly when given.  By default a
+workload first runs 20 probe steps to estimate its step time, then warms up for at
+least 50 ms of steps (the GPU's clocks climb for tens of ms after any idle time,
+the host-side set-up included) and times at least 0.2 s of steps (200 steps at the
+least; 100 for a sub-record), so that the window's first launch and final
+synchronisation are amortised.  The JSON line reports the counts actually run;
+`warmup` includes the probe steps.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -44,6 +53,9 @@ SUB_RECORDS = ["spec8", "spec16", "sweep", "prefill"]
 PERCENTILE_STEPS = 100
 PERCENTILE_SECONDS = 1.0
 PERCENTILE_MAX_STEPS = 20000
+WARMUP_SECONDS = 0.05  # default least span of untimed steps before the timed window
+TIMED_SECONDS = 0.2    # default least span of the timed window
+PROBE_STEPS = 20       # untimed steps that estimate the step time for the defaults
 
 
 def log(*a):
@@ -267,9 +279,10 @@ def roofline(work, kernel_s, traffic):
 
 
 def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks,
-                  percentile_seconds=PERCENTILE_SECONDS):
+                  percentile_seconds=PERCENTILE_SECONDS, min_steps=200, min_warmup=20):
     """Times one workload: steps (two launches each: split-KV + combine), per-step event
-    percentiles, per-launch split events, and back-to-back split launches."""
+    percentiles, per-launch split events, and back-to-back split launches.  steps or
+    warmup None: chosen from the step time (module docstring)."""
     dev = dw.q_nope.device
     ws = mla.new_workspace(dw.B, dw.Sq, dw.H, dw.max_pages, G, device=dev)
     O = torch.empty((dw.B, dw.Sq, dw.H, 512), dtype=torch.float32, device=dev)
@@ -283,6 +296,19 @@ def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks,
         c.splitkv()
         c.combine()
 
+    probe = 0
+    if steps is None or warmup is None:
+        probe = PROBE_STEPS
+        torch.cuda.synchronize()
+        t_probe = time.perf_counter()
+        for i in range(probe):
+            step(i)
+        torch.cuda.synchronize()
+        est = max((time.perf_counter() - t_probe) / probe, 1e-7)
+        if warmup is None:
+            warmup = max(min_warmup, math.ceil(WARMUP_SECONDS / est))
+        if steps is None:
+            steps = max(min_steps, math.ceil(TIMED_SECONDS / est))
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -337,6 +363,8 @@ def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks,
         roof["frac_of_measured_peak"] = round(roof["achieved"] / peaks[key], 4)
         roof["measured_peak_used"] = key
     rec = {
+        "steps": int(steps),
+        "warmup": int(warmup + probe),
         "us_per_step": round(us_step, 2),
         "kv_GBps_per_step": round(work["kv_bytes"] / (us_step * 1e-6) / 1e9, 1),
         "kv_frac_of_hbm_peak": round(work["kv_bytes"] / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -364,12 +392,15 @@ def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks,
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 0.2 s of steps, 200 at the least)")
     ap.add_argument("--percentile-seconds", type=float, default=PERCENTILE_SECONDS,
                     help="least span of steps behind the step percentiles (at least 100 "
                          "steps are always timed); a profiled run passes 0 to keep its "
                          "traces short")
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 50 ms of steps, 20 at the "
+                         "least, after 20 probe steps)")
     ap.add_argument("--config", default="spec4",
                     help="tiny | spec4 | spec8 | spec16 | sweep | prefill")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "e4m3"],
@@ -452,10 +483,10 @@ def main():
     if G > 1 and not args.no_single_pass and not args.nope:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(main_rec["steps"]):
             calls[i % n_copies].single_pass()
         torch.cuda.synchronize()
-        single_pass_us = (time.perf_counter() - t0) * 1e6 / args.steps
+        single_pass_us = (time.perf_counter() - t0) * 1e6 / main_rec["steps"]
         if mla.read_error_flags(ws):
             raise SystemExit("kernel reported a data fault flag")
 
@@ -534,15 +565,15 @@ def main():
             Gs = mla.auto_partitions(dw.B, dw.Sq, dw.H, dw.max_pages)
             log(f"{name}: B={dw.B} Sq={dw.Sq} H={dw.H} kv={dw.kv_bytes() / 1e6:.1f} MB, drawn "
                 f"on the device in {time.perf_counter() - t_gen:.1f}s, partitions={Gs}")
-            sub_steps = 100
-            rec, c2, _, wk = time_workload(torch, np, mla, dw, Gs, sub_steps, 50,
+            rec, c2, _, wk = time_workload(torch, np, mla, dw, Gs, None, None,
                                            stored_traffic(name, "bf16"), peaks,
-                                           args.percentile_seconds)
+                                           args.percentile_seconds, min_steps=100,
+                                           min_warmup=50)
             rec = {"config": {"workload": name, "B": dw.B, "Sq": dw.Sq, "H": dw.H,
                               "context": [int(dw.seq_lens.min()), int(dw.seq_lens.max())],
                               "partitions": Gs, "kv_bytes": wk["kv_bytes"],
                               "tflops_per_step": wk["flops"] / 1e12},
-                   "steps": sub_steps, **rec}
+                   **rec}
             subs[name] = rec
             del c2, dw
             torch.cuda.empty_cache()
@@ -559,8 +590,8 @@ def main():
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": main_rec["steps"],
+        "warmup": main_rec["warmup"],
         "ms_per_step": round(us_step * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
