@@ -278,6 +278,18 @@ def roofline(work, kernel_s, traffic):
             "frac": round(hbm / HBM_PEAK_GBPS, 4), "traffic": traffic}, hbm, tf
 
 
+def default_counts(step_s, steps=None, warmup=None, min_steps=200, min_warmup=20):
+    """(timed steps, untimed steps) for a step time of step_s seconds: an explicit count
+    is kept; otherwise at least WARMUP_SECONDS of untimed and TIMED_SECONDS of timed
+    steps, and never fewer than min_warmup / min_steps."""
+    step_s = max(step_s, 1e-7)
+    if warmup is None:
+        warmup = max(min_warmup, math.ceil(WARMUP_SECONDS / step_s))
+    if steps is None:
+        steps = max(min_steps, math.ceil(TIMED_SECONDS / step_s))
+    return steps, warmup
+
+
 def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks,
                   percentile_seconds=PERCENTILE_SECONDS, min_steps=200, min_warmup=20):
     """Times one workload: steps (two launches each: split-KV + combine), per-step event
@@ -304,11 +316,8 @@ def time_workload(torch, np, mla, dw, G, steps, warmup, traffic, peaks,
         for i in range(probe):
             step(i)
         torch.cuda.synchronize()
-        est = max((time.perf_counter() - t_probe) / probe, 1e-7)
-        if warmup is None:
-            warmup = max(min_warmup, math.ceil(WARMUP_SECONDS / est))
-        if steps is None:
-            steps = max(min_steps, math.ceil(TIMED_SECONDS / est))
+        steps, warmup = default_counts((time.perf_counter() - t_probe) / probe, steps, warmup,
+                                       min_steps, min_warmup)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()

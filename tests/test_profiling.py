@@ -1,6 +1,6 @@
 """Host logic of the measurement tooling (no GPU): rocprofv3 CSV summaries, the
-counter-calibrated traffic per launch, the bench table, and bench.py's lookup of
-stored traffic by workload and pool format."""
+counter-calibrated traffic per launch, the bench table, bench.py's lookup of stored
+traffic by workload and pool format, and its default step counts."""
 import csv
 import importlib.util
 import json
@@ -108,3 +108,17 @@ def test_cpu_baseline_names_its_host():
     model, blas = b.host_cpu_model(), b.blas_name()
     assert model is None or (isinstance(model, str) and model)
     assert blas is None or (isinstance(blas, str) and blas)
+
+
+def test_default_step_counts_follow_the_step_time():
+    """Without --steps/--warmup the bench warms up for at least 50 ms and times at least
+    0.2 s of steps, never fewer than the floors; explicit counts are kept exactly."""
+    b = _bench()
+    steps, warmup = b.default_counts(76e-6)  # a spec4 step
+    assert steps == 2632 and warmup == 658
+    assert steps * 76e-6 >= b.TIMED_SECONDS and warmup * 76e-6 >= b.WARMUP_SECONDS
+    assert b.default_counts(10e-3) == (200, 20)  # a prefill step: the floors
+    assert b.default_counts(1.15e-3, min_steps=100, min_warmup=50) == (174, 50)
+    assert b.default_counts(76e-6, steps=50, warmup=5) == (50, 5)
+    assert b.default_counts(76e-6, steps=7) == (7, 658)
+    assert b.default_counts(0.0)[0] >= 200  # a zero estimate cannot divide by zero
